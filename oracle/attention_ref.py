@@ -1,0 +1,185 @@
+"""Plain fp64 CPU oracle for multi-head scaled dot-product attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or run
+this module: only the tests, the smoke check and the bench's CPU-baseline leg
+use it. It shares no code with the HIP library or its Python binding.
+
+What it computes is the pages' definition written out, one step at a time,
+in float64, materialising the full score matrix:
+
+* Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V, the softmax taken over
+  each row (one query against all keys) -- "The Transformer"
+  (hoshank.vercel.app), "The Mathematics", the Attention equation and its
+  symbol table; the same formula in "How Transformers Work"
+  (worksonmygpu.com), "Scaled dot-product attention", steps 1-4.
+* MultiHead(Q, K, V) = Concat(head_1..head_h) W^O with
+  head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V) -- same page, the MultiHead
+  equation; the split into h contiguous column blocks and the concat in head
+  order follow the multi_head snippet of "32 Transformer"
+  (ml-canon-en.vercel.app), "PyTorch Implementation".
+* The causal mask is an additive matrix, 0 on and below the diagonal and -inf
+  above it, added to the scores before the softmax, so a blocked key gets a
+  weight of exactly 0 -- "The Transformer" (rayaq.ca), "Masks: who may look at
+  whom", with its printed 4x4 example.
+
+Readings where the pages are silent (each is listed in the design notes):
+the softmax subtracts the row maximum before exponentiating (softmax is
+unchanged by a per-row shift; it only avoids overflow); no biases in the
+projections; weights are stored (in, out) so Q = X W; the mask is only
+defined for N_q == N_k.
+
+Every function here is pinned by tests/test_oracle.py against properties the
+pages fix (rows sum to 1, permutation equivariance, the printed mask, closed
+forms, brute force on tiny inputs, an independent library routine).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def causal_mask(n: int) -> np.ndarray:
+    """Additive causal mask: 0 where key j <= query i, -inf where j > i.
+
+    "The Transformer" (rayaq.ca), "Masks: who may look at whom": the decoder's
+    mask is the strictly upper triangle filled with -inf, diagonal kept.
+    """
+    m = np.zeros((n, n), dtype=np.float64)
+    for i in range(n):
+        for j in range(i + 1, n):
+            m[i, j] = -np.inf
+    return m
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row-wise softmax over the last axis: each row becomes weights summing to 1.
+
+    "The Transformer" (hoshank.vercel.app), "The Mathematics", symbol table
+    entry for softmax. Subtracting the row maximum first leaves the result
+    unchanged and keeps exp() finite.
+    """
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention_weights_ref(q: np.ndarray, k: np.ndarray, *, causal: bool = False,
+                          scale: float | None = None, rows=None) -> np.ndarray:
+    """P = softmax(scale * Q K^T (+ causal mask)) for one (batch, head).
+
+    q: (N_q, d_k), k: (N_k, d_k). rows: optional query positions; only those
+    rows of P are formed, each one complete over all keys.
+    Default scale is 1/sqrt(d_k) ("The Transformer" (hoshank.vercel.app),
+    "The Mathematics"; "32 Transformer", "Why we divide by sqrt(dk)").
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    d_k = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    pos = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    s = np.matmul(q[pos], k.T) * scale            # every query dotted with every key
+    if causal:
+        if q.shape[0] != k.shape[0]:
+            raise ValueError("the causal mask is defined for N_q == N_k only")
+        s = s + causal_mask(k.shape[0])[pos]
+    return softmax_rows(s)
+
+
+def attention_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool = False,
+                  scale: float | None = None, rows=None):
+    """O = softmax(scale * Q K^T (+ mask)) V over every (batch, head).
+
+    q: (B, H, N_q, d_k), k: (B, H, N_k, d_k), v: (B, H, N_k, d_v); any float
+    dtype, widened exactly to float64. rows: optional sorted query positions
+    (the same for every (b, h)); the outputs then hold only those rows.
+
+    Returns (O, rowsum, lse):
+      O      (B, H, R, d_v)  attention output
+      rowsum (B, H, R)       sum of each weight row (1 up to rounding)
+      lse    (B, H, R)       natural log of sum_j exp(scale * q_i . k_j) over
+                             the unmasked keys
+    The weighted sum of values: "How Transformers Work", "Scaled dot-product
+    attention", step 4.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, n_q, d_k = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    R = n_q if rows is None else len(rows)
+    o = np.empty((B, H, R, v.shape[-1]), dtype=np.float64)
+    rowsum = np.empty((B, H, R), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    pos = np.arange(n_q) if rows is None else np.asarray(rows)
+    for b in range(B):
+        for h in range(H):
+            s = np.matmul(q[b, h][pos], k[b, h].T) * scale
+            if causal:
+                if n_q != k.shape[2]:
+                    raise ValueError("the causal mask is defined for N_q == N_k only")
+                s = s + causal_mask_rows(k.shape[2], pos)
+            m = np.max(s, axis=-1, keepdims=True)
+            e = np.exp(s - m)
+            l = np.sum(e, axis=-1, keepdims=True)
+            p = e / l
+            o[b, h] = np.matmul(p, v[b, h])
+            rowsum[b, h] = np.sum(p, axis=-1)
+            lse[b, h] = (m + np.log(l))[:, 0]
+    return o, rowsum, lse
+
+
+def causal_mask_rows(n: int, rows) -> np.ndarray:
+    """The rows `rows` of causal_mask(n), formed without the full n x n matrix."""
+    rows = np.asarray(rows)
+    j = np.arange(n)[None, :]
+    out = np.zeros((len(rows), n), dtype=np.float64)
+    out[j > rows[:, None]] = -np.inf
+    return out
+
+
+def split_heads(t: np.ndarray, heads: int) -> np.ndarray:
+    """(B, N, h*d) -> (B, h, N, d): head i takes columns [i*d, (i+1)*d).
+
+    "32 Transformer", "PyTorch Implementation": view(seq, h, -1) then
+    transpose, per batch item.
+    """
+    B, N, D = t.shape
+    return t.reshape(B, N, heads, D // heads).transpose(0, 2, 1, 3)
+
+
+def concat_heads(t: np.ndarray) -> np.ndarray:
+    """(B, h, N, d) -> (B, N, h*d), heads side by side in order."""
+    B, H, N, d = t.shape
+    return t.transpose(0, 2, 1, 3).reshape(B, N, H * d)
+
+
+def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: np.ndarray,
+            wv: np.ndarray, wo: np.ndarray, heads: int, *, causal: bool = False,
+            rows=None) -> np.ndarray:
+    """MultiHead(Xq, Xk, Xv) = Concat(head_1..head_h) W^O, no biases.
+
+    xq: (B, N_q, d_model); xk, xv: (B, N_k, d_model); w*: (d_model, d_model)
+    stored (in, out). Scale is 1/sqrt(d_model / heads).
+    "The Transformer" (hoshank.vercel.app), "The Mathematics", MultiHead
+    equation; "32 Transformer", "PyTorch Implementation", multi_head.
+    Self-attention passes the same x three times; cross-attention passes the
+    decoder state as xq and the encoder memory as xk and xv ("The Transformer"
+    (rayaq.ca), "The decoder stack").
+    rows: optional query positions; only those output rows are returned.
+    """
+    xq = np.asarray(xq, dtype=np.float64)
+    xk = np.asarray(xk, dtype=np.float64)
+    xv = np.asarray(xv, dtype=np.float64)
+    d_model = xq.shape[-1]
+    if d_model % heads:
+        raise ValueError("d_model must be divisible by the number of heads")
+    q = np.matmul(xq, np.asarray(wq, dtype=np.float64))
+    k = np.matmul(xk, np.asarray(wk, dtype=np.float64))
+    v = np.matmul(xv, np.asarray(wv, dtype=np.float64))
+    qh, kh, vh = split_heads(q, heads), split_heads(k, heads), split_heads(v, heads)
+    o, _, _ = attention_ref(qh, kh, vh, causal=causal, scale=1.0 / math.sqrt(d_model // heads),
+                            rows=rows)
+    return np.matmul(concat_heads(o), np.asarray(wo, dtype=np.float64))

@@ -1,0 +1,397 @@
+"""Pins for the fp64 oracle: properties and values the pages and mathematics fix.
+
+Each check takes the attention function under test (signature of
+oracle.attention_ref) and, where needed, the multi-head function (signature of
+oracle.mha_ref), and raises AssertionError when the property fails. The
+pin tests run them on the oracle; the mutant tests run them on deliberately
+broken copies of the oracle to show that each plausible mistake is caught.
+
+Pages cited: "32 Transformer" (ml-canon-en.vercel.app); "How Transformers Work"
+(worksonmygpu.com); "The Transformer" (hoshank.vercel.app); "Transformer: The
+Starting Point of Everything" (chenyuan1125.github.io); "The Transformer"
+(rayaq.ca).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _qkv(seed, B=2, H=3, nq=7, nk=7, d=5, dv=None):
+    r = _rng(seed)
+    dv = d if dv is None else dv
+    return (r.standard_normal((B, H, nq, d)), r.standard_normal((B, H, nk, d)),
+            r.standard_normal((B, H, nk, dv)))
+
+
+def read_golden_matrix(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append([float(t) for t in line.split()])
+    return np.array(rows)
+
+
+def read_golden_table(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split()
+            out[key] = int(val)
+    return out
+
+
+# ------------------------------------------------------------------ P1 rows sum to 1
+def check_rows_sum_to_one(attn):
+    """Softmax rows are probability distributions ("The Transformer"
+    (hoshank.vercel.app), "The Mathematics", softmax row of the symbol table).
+    Checked with V = identity so that O *is* the weight matrix, independently
+    of the rowsum the function reports."""
+    for causal in (False, True):
+        q, k, _ = _qkv(11)
+        n = k.shape[2]
+        eye = np.broadcast_to(np.eye(n), (q.shape[0], q.shape[1], n, n)).copy()
+        p, rowsum, _ = attn(q, k, eye, causal=causal)
+        assert np.all(p >= 0), "negative attention weight"
+        assert np.allclose(p.sum(-1), 1.0, rtol=0, atol=1e-12), "weight rows do not sum to 1"
+        assert np.allclose(rowsum, 1.0, rtol=0, atol=1e-12), "reported row sums differ from 1"
+
+
+# ------------------------------------------------------------------ P2 permutation equivariance
+def check_permutation_equivariance(attn):
+    """Swapping tokens swaps the outputs and changes nothing else ("The
+    Transformer" (rayaq.ca), "Embeddings and positions"); permuting keys and
+    values together leaves every output unchanged ("32 Transformer",
+    "Positional encodings": attention alone knows no order)."""
+    q, k, v = _qkv(12, nq=9, nk=9)
+    perm = _rng(13).permutation(9)
+    o, _, _ = attn(q, k, v)
+    o_p, _, _ = attn(q[:, :, perm], k[:, :, perm], v[:, :, perm])
+    assert np.allclose(o_p, o[:, :, perm], rtol=0, atol=1e-12), "not permutation-equivariant"
+    o_kv, _, _ = attn(q, k[:, :, perm], v[:, :, perm])
+    assert np.allclose(o_kv, o, rtol=0, atol=1e-12), "key/value order changed the output"
+
+
+# ------------------------------------------------------------------ P3 convex combination
+def check_constant_v_and_convex_hull(attn):
+    """Weights are >= 0 and sum to 1, so O is a convex combination of V's rows:
+    constant V gives constant O, and every O lies between min and max of V."""
+    q, k, v = _qkv(14, nq=8, nk=8)
+    c = _rng(15).standard_normal(v.shape[-1])
+    vc = np.broadcast_to(c, v.shape).copy()
+    for causal in (False, True):
+        o, _, _ = attn(q, k, vc, causal=causal)
+        assert np.allclose(o, np.broadcast_to(c, o.shape), rtol=0, atol=1e-12), "constant V not kept"
+    o, _, _ = attn(q, k, v)
+    lo = v.min(axis=2, keepdims=True)
+    hi = v.max(axis=2, keepdims=True)
+    assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12), "output outside the hull of V"
+
+
+# ------------------------------------------------------------------ P4 causal locality
+def check_causal_locality(attn):
+    """With the causal mask, output row i depends only on rows <= i ("How
+    Transformers Work", "What changed since 2017"; "The Transformer"
+    (hoshank.vercel.app), "The Breakthrough": the mask removes future
+    positions). Perturbing rows > i of Q, K and V must leave rows <= i
+    bitwise unchanged."""
+    q, k, v = _qkv(16, nq=10, nk=10)
+    o, _, _ = attn(q, k, v, causal=True)
+    for i in (0, 3, 8):
+        r = _rng(17 + i)
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        q2[:, :, i + 1:] += r.standard_normal(q2[:, :, i + 1:].shape)
+        k2[:, :, i + 1:] += r.standard_normal(k2[:, :, i + 1:].shape)
+        v2[:, :, i + 1:] += r.standard_normal(v2[:, :, i + 1:].shape)
+        o2, _, _ = attn(q2, k2, v2, causal=True)
+        assert np.array_equal(o2[:, :, :i + 1], o[:, :, :i + 1]), f"row <= {i} saw the future"
+    # and the mask does matter: without it, row 0 changes when later keys change
+    o_full, _, _ = attn(q, k, v, causal=False)
+    assert not np.allclose(o_full[:, :, 0], o[:, :, 0]), "causal flag had no effect"
+
+
+# ------------------------------------------------------------------ P5 the printed mask
+def check_printed_mask(mask_fn):
+    """The mask for n = 4 equals the tensor printed on "The Transformer"
+    (rayaq.ca), "Masks: who may look at whom"."""
+    want = read_golden_matrix("causal_mask_n4.txt")
+    got = mask_fn(4)
+    assert got.shape == want.shape
+    assert np.array_equal(np.isinf(got), np.isinf(want)), "mask pattern differs from the page"
+    assert np.all(got[np.isfinite(want)] == 0)
+    assert np.all(got[np.isinf(want)] < 0)
+
+
+def check_masked_weight_is_zero(attn):
+    """A blocked key gets a weight of exactly 0 ("The Transformer" (rayaq.ca),
+    "Masks"): with V = identity the strict upper triangle of O is 0."""
+    q, k, _ = _qkv(18, nq=6, nk=6)
+    eye = np.broadcast_to(np.eye(6), (2, 3, 6, 6)).copy()
+    p, _, _ = attn(q, k, eye, causal=True)
+    iu = np.triu_indices(6, 1)
+    assert np.all(p[:, :, iu[0], iu[1]] == 0.0), "masked weight not exactly zero"
+    assert np.all(p[:, :, np.arange(6), np.arange(6)] > 0), "diagonal must stay visible"
+
+
+# ------------------------------------------------------------------ P6 closed forms
+def check_closed_forms(attn):
+    q, k, v = _qkv(19, nq=5, nk=5)
+    # one key: the only weight is 1, O = V
+    o, _, _ = attn(q, k[:, :, :1], v[:, :, :1])
+    assert np.allclose(o, np.broadcast_to(v[:, :, :1], o.shape), rtol=0, atol=1e-14), "N_k = 1"
+    # zero queries: uniform weights, O = mean of V (unmasked), prefix mean (causal)
+    z = np.zeros_like(q)
+    o, _, _ = attn(z, k, v)
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), atol=1e-14)
+    o, _, _ = attn(z, k, v, causal=True)
+    prefix = np.cumsum(v, axis=2) / np.arange(1, 6)[None, None, :, None]
+    assert np.allclose(o, prefix, rtol=0, atol=1e-14), "causal prefix mean"
+    # scale 0 gives uniform weights too
+    o, _, _ = attn(q, k, v, scale=0.0)
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), atol=1e-14)
+    # causal row 0 sees only key 0
+    o, _, _ = attn(q, k, v, causal=True)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0]), "causal row 0 must equal V_0"
+    # all keys equal: uniform weights
+    ke = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    o, _, _ = attn(q, ke, v)
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), atol=1e-14)
+    # two keys: weight of key 1 is the logistic function of the scaled score gap
+    q1, k2, v2 = q[:, :, :3], k[:, :, :2], np.zeros((2, 3, 2, 1))
+    v2[:, :, 0, 0] = 1.0
+    o, _, _ = attn(q1, k2, v2)
+    s = np.einsum("bhid,bhjd->bhij", q1, k2) / math.sqrt(q.shape[-1])
+    want = 1.0 / (1.0 + np.exp(-(s[..., 0] - s[..., 1])))
+    assert np.allclose(o[..., 0], want, rtol=0, atol=1e-14), "two-key logistic form"
+
+
+# ------------------------------------------------------------------ P7 temperature
+def check_low_temperature_argmax(attn):
+    """A large scale (low temperature) collapses each row onto its single best
+    key ("The Transformer" (rayaq.ca), "Worked example")."""
+    q, k, v = _qkv(20, nq=6, nk=12)
+    s = np.einsum("bhid,bhjd->bhij", q, k)
+    srt = np.sort(s, axis=-1)
+    gap = srt[..., -1] - srt[..., -2]
+    assert gap.min() > 1e-3  # inputs chosen without near ties
+    o, _, _ = attn(q, k, v, scale=1e5)
+    best = np.argmax(s, axis=-1)
+    want = np.take_along_axis(v, best[..., None], axis=2)
+    assert np.allclose(o, want, rtol=0, atol=1e-12), "low temperature must pick the best key"
+
+
+# ------------------------------------------------------------------ P8 the scale divides by sqrt(d_k)
+def check_default_scale(attn):
+    """The default scale divides the scores by sqrt(d_k) ("32 Transformer",
+    "Why we divide by sqrt(dk)"; "The Transformer" (hoshank.vercel.app), "The
+    Mathematics"). With two keys, log(w1/w2) recovers the scaled score gap; for
+    unit-normal q, k in d_k = 64 that gap has variance 2 (two unit-variance
+    scaled scores), not 2 * 64."""
+    d = 64
+    r = _rng(21)
+    q = r.standard_normal((1, 1, 4096, d))
+    k = r.standard_normal((1, 1, 2, d))
+    v = np.zeros((1, 1, 2, 1))
+    v[..., 0, 0] = 1.0
+    o, _, _ = attn(q, k, v)
+    w1 = o[0, 0, :, 0]
+    gap = np.log(w1) - np.log1p(-w1)
+    want = (q[0, 0] @ (k[0, 0, 0] - k[0, 0, 1])) / math.sqrt(d)
+    assert np.allclose(gap, want, rtol=1e-9, atol=1e-9), "score gap is not q.(k1-k2)/sqrt(d)"
+    # the page's variance argument: with unit-normal queries the scaled gap has
+    # variance |k1 - k2|^2 / d_k (about 2 here), i.e. unit variance per scaled score
+    ratio = gap.var() / (np.sum((k[0, 0, 0] - k[0, 0, 1]) ** 2) / d)
+    assert 0.9 < ratio < 1.1, "scaled scores do not have unit variance"
+
+
+# ------------------------------------------------------------------ P10 brute force and a hand example
+def _brute_attention(q, k, v, causal, scale):
+    """Pure-Python loops with math.exp, one query at a time."""
+    nq, nk, d, dv = len(q), len(k), len(q[0]), len(v[0])
+    out = []
+    for i in range(nq):
+        scores = []
+        for j in range(nk):
+            if causal and j > i:
+                scores.append(None)
+                continue
+            scores.append(scale * sum(q[i][t] * k[j][t] for t in range(d)))
+        finite = [s for s in scores if s is not None]
+        m = max(finite)
+        w = [0.0 if s is None else math.exp(s - m) for s in scores]
+        tot = sum(w)
+        out.append([sum(w[j] / tot * v[j][c] for j in range(nk)) for c in range(dv)])
+    return out
+
+
+def check_brute_force(attn):
+    r = _rng(22)
+    for trial in range(12):
+        n = int(r.integers(1, 5))
+        nk = n if trial % 2 else int(r.integers(1, 5))
+        d = int(r.integers(1, 4))
+        causal = bool(trial % 2)
+        q = r.integers(-3, 4, size=(n, d)).astype(float)
+        k = r.integers(-3, 4, size=(nk, d)).astype(float)
+        v = r.integers(-3, 4, size=(nk, 2)).astype(float)
+        want = _brute_attention(q.tolist(), k.tolist(), v.tolist(), causal, 1 / math.sqrt(d))
+        got, _, _ = attn(q[None, None], k[None, None], v[None, None], causal=causal)
+        assert np.allclose(got[0, 0], np.array(want), rtol=0, atol=1e-12), f"brute force trial {trial}"
+
+
+def check_hand_example(attn):
+    """q = (1, 0); k1 = (1, 0); k2 = (0, 1); d = 2. Scores 1/sqrt(2) and 0, so the
+    weights are sigma(1/sqrt(2)) and 1 - sigma(1/sqrt(2)), worked by hand."""
+    q = np.array([[[[1.0, 0.0]]]])
+    k = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    v = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    o, _, lse = attn(q, k, v)
+    w1 = 1.0 / (1.0 + math.exp(-1.0 / math.sqrt(2.0)))
+    assert abs(o[0, 0, 0, 0] - w1) < 1e-15 and abs(o[0, 0, 0, 1] - (1 - w1)) < 1e-15
+    assert abs(lse[0, 0, 0] - math.log(math.exp(1 / math.sqrt(2)) + 1.0)) < 1e-15
+
+
+# ------------------------------------------------------------------ P11 linearity and shift invariance
+def check_linearity_and_shift(attn):
+    q, k, v = _qkv(23)
+    v2 = _qkv(24)[2]
+    a, b = 1.7, -0.4
+    o1, _, _ = attn(q, k, v)
+    o2, _, _ = attn(q, k, v2)
+    o12, _, _ = attn(q, k, a * v + b * v2)
+    assert np.allclose(o12, a * o1 + b * o2, rtol=0, atol=1e-12), "not linear in V"
+    c = _rng(25).standard_normal(k.shape[-1])
+    for causal in (False, True):
+        o, _, _ = attn(q, k, v, causal=causal)
+        os_, _, _ = attn(q, k + c, v, causal=causal)
+        assert np.allclose(os_, o, rtol=0, atol=1e-12), "shifting every key changed O"
+
+
+# ------------------------------------------------------------------ P12 multi-head structure
+def check_mha_structure(mha, attn):
+    r = _rng(26)
+    B, N, dm = 2, 5, 6
+    x = r.standard_normal((B, N, dm))
+    # h = 1 with identity weights is plain attention on x
+    eye = np.eye(dm)
+    o = mha(x, x, x, eye, eye, eye, eye, 1)
+    want, _, _ = attn(x[:, None], x[:, None], x[:, None])
+    assert np.allclose(o, want[:, 0], rtol=0, atol=1e-12), "h=1, W=I is not attention(x,x,x)"
+    # block decomposition: out = sum_i head_i @ W^O[i*d:(i+1)*d]
+    h, d = 3, 2
+    wq, wk, wv, wo = (r.standard_normal((dm, dm)) for _ in range(4))
+    # cross-attention with N_k != N_q, and with three distinct inputs of equal length
+    for xk, xv in ((r.standard_normal((B, 4, dm)),) * 2,
+                   (r.standard_normal((B, N, dm)), r.standard_normal((B, N, dm)))):
+        out = mha(x, xk, xv, wq, wk, wv, wo, h)
+        acc = np.zeros_like(out)
+        for i in range(h):
+            cols = slice(i * d, (i + 1) * d)
+            head, _, _ = attn((x @ wq[:, cols])[:, None], (xk @ wk[:, cols])[:, None],
+                              (xv @ wv[:, cols])[:, None])
+            acc += head[:, 0] @ wo[cols, :]
+        assert np.allclose(out, acc, rtol=0, atol=1e-12), "head split/concat order, W orientation or inputs"
+
+
+# ------------------------------------------------------------------ P9 an independent library routine
+def check_torch_sdpa(attn, mha):
+    """torch's CPU float64 scaled_dot_product_attention and nn.MultiheadAttention
+    compute the same definition ("The Transformer" (rayaq.ca), "Attention, by
+    hand" and "In PyTorch"). Used as a cross-check only."""
+    import torch
+    import torch.nn.functional as F
+    q, k, v = _qkv(27, nq=6, nk=9, d=4, dv=3)
+    o, _, _ = attn(q, k, v)
+    t = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v))
+    assert np.allclose(o, t.numpy(), rtol=0, atol=1e-12), "differs from torch sdpa"
+    q, k, v = _qkv(28, nq=7, nk=7, d=4)
+    o, _, _ = attn(q, k, v, causal=True)
+    t = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                       is_causal=True)
+    assert np.allclose(o, t.numpy(), rtol=0, atol=1e-12), "differs from torch causal sdpa"
+    r = _rng(29)
+    B, N, M, dm, h = 2, 5, 7, 8, 2
+    xq, xkv = r.standard_normal((B, N, dm)), r.standard_normal((B, M, dm))
+    wq, wk, wv, wo = (r.standard_normal((dm, dm)) for _ in range(4))
+    m = torch.nn.MultiheadAttention(dm, h, bias=False, batch_first=True).double()
+    with torch.no_grad():
+        m.in_proj_weight.copy_(torch.from_numpy(np.concatenate([wq.T, wk.T, wv.T])))
+        m.out_proj.weight.copy_(torch.from_numpy(wo.T))
+    m.eval()
+    with torch.no_grad():
+        t, _ = m(torch.from_numpy(xq), torch.from_numpy(xkv), torch.from_numpy(xkv), need_weights=False)
+    got = mha(xq, xkv, xkv, wq, wk, wv, wo, h)
+    assert np.allclose(got, t.numpy(), rtol=0, atol=1e-12), "differs from nn.MultiheadAttention"
+
+
+# ------------------------------------------------------------------ P13 projection shapes
+def check_parameter_counts(mha):
+    """A bias-free MHA at the base width holds 4 * d_model^2 weights; adding the
+    biases, the FFN and the two LayerNorms of one encoder layer gives the
+    count printed on "The Transformer" (rayaq.ca), "In PyTorch"."""
+    sizes = read_golden_table("model_sizes.txt")
+    dm, h, ff = sizes["base_d_model"], sizes["base_heads"], sizes["ffn_inner"]
+    assert dm // h == sizes["base_d_k"] == sizes["base_d_v"]
+    assert sizes["big_d_model"] // sizes["big_heads"] == sizes["base_d_k"]
+    # the oracle's multi-head function takes four (d_model, d_model) matrices
+    r = _rng(30)
+    x = r.standard_normal((1, 3, dm))
+    ws = [r.standard_normal((dm, dm)) / math.sqrt(dm) for _ in range(4)]
+    assert mha(x, x, x, *ws, h).shape == (1, 3, dm)
+    mha_weights = sum(w.size for w in ws)
+    assert mha_weights == 4 * dm * dm == 1_048_576
+    with_bias = mha_weights + 4 * dm
+    ffn = dm * ff + ff + ff * dm + dm
+    norms = 2 * 2 * dm
+    assert with_bias + ffn + norms == sizes["encoder_layer_params"]
+
+
+# ------------------------------------------------------------------ sampled rows agree with full rows
+def check_rows_subset(attn, mha):
+    q, k, v = _qkv(31, nq=12, nk=12)
+    rows = np.array([0, 5, 11])
+    for causal in (False, True):
+        full, rs, lse = attn(q, k, v, causal=causal)
+        part, rs2, lse2 = attn(q, k, v, causal=causal, rows=rows)
+        assert np.allclose(part, full[:, :, rows], rtol=0, atol=1e-14)
+        assert np.allclose(lse2, lse[:, :, rows], rtol=0, atol=1e-14)
+    r = _rng(32)
+    x = r.standard_normal((2, 12, 6))
+    ws = [r.standard_normal((6, 6)) for _ in range(4)]
+    for causal in (False, True):
+        full = mha(x, x, x, *ws, 3, causal=causal)
+        part = mha(x, x, x, *ws, 3, causal=causal, rows=rows)
+        assert np.allclose(part, full[:, rows], rtol=0, atol=1e-12)
+
+
+def check_lse(attn):
+    """lse_i = log sum_j exp(scale * q_i . k_j) over the unmasked keys."""
+    q, k, v = _qkv(33, nq=5, nk=5, d=3)
+    for causal in (False, True):
+        _, _, lse = attn(q, k, v, causal=causal)
+        s = np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(3)
+        if causal:
+            s = np.where(np.triu(np.ones((5, 5), bool), 1), -np.inf, s)
+        want = np.log(np.sum(np.exp(s), axis=-1))
+        assert np.allclose(lse, want, rtol=0, atol=1e-13), "lse"
+
+
+ATTENTION_PINS = [check_rows_sum_to_one, check_permutation_equivariance,
+                  check_constant_v_and_convex_hull, check_causal_locality,
+                  check_masked_weight_is_zero, check_closed_forms, check_low_temperature_argmax,
+                  check_default_scale, check_brute_force, check_hand_example,
+                  check_linearity_and_shift, check_lse]

@@ -1,0 +1,59 @@
+"""The fp64 oracle against what the pages and mathematics fix (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+
+@pytest.mark.parametrize("check", pins.ATTENTION_PINS, ids=lambda f: f.__name__)
+def test_attention_pin(check):
+    check(oracle.attention_ref)
+
+
+def test_printed_mask():
+    pins.check_printed_mask(oracle.causal_mask)
+
+
+def test_mask_rows_match_full_mask():
+    full = oracle.causal_mask(9)
+    rows = np.array([0, 4, 8])
+    assert np.array_equal(oracle.causal_mask_rows(9, rows), full[rows])
+
+
+def test_weights_function_matches_attention():
+    r = np.random.default_rng(3)
+    q, k = r.standard_normal((6, 4)), r.standard_normal((6, 4))
+    for causal in (False, True):
+        p = oracle.attention_weights_ref(q, k, causal=causal)
+        o, _, _ = oracle.attention_ref(q[None, None], k[None, None], np.eye(6)[None, None], causal=causal)
+        assert np.allclose(p, o[0, 0], rtol=0, atol=1e-14)
+    # with all-zero scores the causal weights are uniform over the visible keys,
+    # and their zero pattern is the printed mask's -inf pattern
+    p = oracle.attention_weights_ref(np.zeros((4, 1)), np.zeros((4, 1)), causal=True)
+    want = pins.read_golden_matrix("causal_mask_n4.txt")
+    assert np.array_equal(p == 0, np.isinf(want))
+    assert np.allclose(p.sum(1), 1.0) and np.allclose(p[3], 0.25)
+
+
+def test_mha_structure():
+    pins.check_mha_structure(oracle.mha_ref, oracle.attention_ref)
+
+
+def test_rows_subset():
+    pins.check_rows_subset(oracle.attention_ref, oracle.mha_ref)
+
+
+def test_parameter_counts():
+    pins.check_parameter_counts(oracle.mha_ref)
+
+
+def test_torch_cross_check():
+    pins.check_torch_sdpa(oracle.attention_ref, oracle.mha_ref)
+
+
+def test_causal_rejects_cross_shapes():
+    r = np.random.default_rng(4)
+    q, k = r.standard_normal((1, 1, 3, 2)), r.standard_normal((1, 1, 5, 2))
+    with pytest.raises(ValueError):
+        oracle.attention_ref(q, k, k, causal=True)

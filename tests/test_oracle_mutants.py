@@ -1,0 +1,135 @@
+"""Plant plausible mistakes in a copy of the oracle and show the pins catch each.
+
+The mutants live here, on the CPU, and never touch the GPU path. Each one is
+the plain definition with exactly one mistake; the test passes when at least
+one pin rejects the mutant (an AssertionError, or arithmetic that breaks, e.g.
+a row left with no visible key).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+
+def _mutant_attention(mutation):
+    def attn(q, k, v, *, causal=False, scale=None, rows=None):
+        q = np.asarray(q, np.float64)
+        k = np.asarray(k, np.float64)
+        v = np.asarray(v, np.float64)
+        B, H, nq, d = q.shape
+        nk = k.shape[2]
+        if scale is None:
+            scale = {"scale_times_sqrt_d": math.sqrt(d), "no_scale": 1.0,
+                     "scale_one_over_d": 1.0 / d}.get(mutation, 1.0 / math.sqrt(d))
+        pos = np.arange(nq) if rows is None else np.asarray(rows)
+        o = np.empty((B, H, len(pos), v.shape[-1]))
+        rs = np.empty((B, H, len(pos)))
+        lse = np.empty((B, H, len(pos)))
+        for b in range(B):
+            for h in range(H):
+                kk = k[b, h]
+                s = q[b, h][pos] @ kk.T * scale
+                if mutation == "sign_flip":
+                    s = -s
+                if causal:
+                    i = pos[:, None]
+                    j = np.arange(nk)[None, :]
+                    blocked = {"mask_flipped": j < i, "mask_no_diagonal": j >= i,
+                               "mask_off_by_one": j > i + 1}.get(mutation, j > i)
+                    if mutation == "mask_after_softmax":
+                        pass
+                    else:
+                        s = np.where(blocked, -np.inf, s)
+                axis = -2 if mutation == "softmax_wrong_axis" else -1
+                m = np.max(s, axis=axis, keepdims=True)
+                e = np.exp(s - m)
+                l = np.sum(e, axis=axis, keepdims=True)
+                p = e if mutation == "no_normalise" else e / l
+                if causal and mutation == "mask_after_softmax":
+                    p = np.where(np.arange(nk)[None, :] > pos[:, None], 0.0, p)
+                vv = kk[:, :v.shape[-1]] if mutation == "uses_k_for_v" else v[b, h]
+                if mutation == "transposed_p" and p.shape[0] == p.shape[1]:
+                    p = p.T
+                o[b, h] = p @ vv
+                rs[b, h] = p.sum(-1)
+                lse[b, h] = (m + np.log(l))[:, 0] if axis == -1 else np.log(np.exp(s).sum(-1))
+        return o, rs, lse
+    return attn
+
+
+ATTENTION_MUTANTS = ["scale_times_sqrt_d", "no_scale", "scale_one_over_d", "sign_flip",
+                     "mask_flipped", "mask_no_diagonal", "mask_off_by_one", "mask_after_softmax",
+                     "softmax_wrong_axis", "no_normalise", "uses_k_for_v", "transposed_p"]
+
+
+def _caught(fn):
+    import warnings
+    try:
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            with np.errstate(all="ignore"):
+                fn()
+    except (AssertionError, ValueError, FloatingPointError, IndexError):
+        return True
+    return False
+
+
+@pytest.mark.parametrize("mutation", ATTENTION_MUTANTS)
+def test_attention_mutant_is_caught(mutation):
+    attn = _mutant_attention(mutation)
+    caught = [c.__name__ for c in pins.ATTENTION_PINS if _caught(lambda c=c: c(attn))]
+    assert caught, f"no pin catches the mutant {mutation!r}"
+
+
+def _mutant_mha(mutation):
+    def mha(xq, xk, xv, wq, wk, wv, wo, heads, *, causal=False, rows=None):
+        xq, xk, xv = (np.asarray(t, np.float64) for t in (xq, xk, xv))
+        wq, wk, wv, wo = (np.asarray(t, np.float64) for t in (wq, wk, wv, wo))
+        if mutation == "weights_transposed":
+            wq, wk, wv, wo = wq.T, wk.T, wv.T, wo.T
+        B, N, dm = xq.shape
+        d = dm // heads
+
+        def split(t):
+            b, n, _ = t.shape
+            if mutation == "heads_interleaved":
+                return t.reshape(b, n, d, heads).transpose(0, 3, 1, 2)
+            return t.reshape(b, n, heads, d).transpose(0, 2, 1, 3)
+
+        q, k, v = split(xq @ wq), split(xk @ wk), split(xv @ wv)
+        if mutation == "value_from_query_input":
+            v = split(xq @ wv)
+        o, _, _ = oracle.attention_ref(q, k, v, causal=causal, scale=1 / math.sqrt(d), rows=rows)
+        if mutation == "concat_reversed":
+            o = o[:, ::-1]
+        cat = o.transpose(0, 2, 1, 3).reshape(B, o.shape[2], dm)
+        if mutation == "no_output_projection":
+            return cat
+        return cat @ wo
+    return mha
+
+
+MHA_MUTANTS = ["weights_transposed", "heads_interleaved", "concat_reversed",
+               "no_output_projection", "value_from_query_input"]
+
+
+@pytest.mark.parametrize("mutation", MHA_MUTANTS)
+def test_mha_mutant_is_caught(mutation):
+    mha = _mutant_mha(mutation)
+    checks = [lambda: pins.check_mha_structure(mha, oracle.attention_ref),
+              lambda: pins.check_torch_sdpa(oracle.attention_ref, mha),
+              lambda: pins.check_parameter_counts(mha)]
+    assert any(_caught(c) for c in checks), f"no pin catches the mutant {mutation!r}"
+
+
+def test_unmutated_copies_pass():
+    """The mutant scaffolding itself, with no mistake planted, passes every pin."""
+    attn = _mutant_attention("none")
+    for c in pins.ATTENTION_PINS:
+        c(attn)
+    mha = _mutant_mha("none")
+    pins.check_mha_structure(mha, oracle.attention_ref)
+    pins.check_torch_sdpa(oracle.attention_ref, mha)

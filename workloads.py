@@ -1,0 +1,198 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module only draws and stores numbers. It holds none of the attention
+arithmetic: no products, no softmax, no masking. Both the fp64 oracle and the
+HIP path receive exactly the arrays produced here, so any disagreement between
+them is compute error, never input error.
+
+Shapes follow the pages' base model (d_model = 512, h = 8, d_k = d_v = 64;
+"The Transformer", hoshank.vercel.app, "The Mathematics", symbol tables under
+the Attention and MultiHead equations) and the big model's head count for the
+long causal case (width 1024 with 16 heads, same section). Values are unit
+normal, the variance that the scale argument assumes ("32 Transformer",
+ml-canon-en.vercel.app, "Why we divide by sqrt(dk)"). Projection weights are
+N(0, 1/d_model) so that the projected Q, K and V stay unit variance.
+
+Recipe, per workload: ``numpy.random.default_rng(seed)`` (PCG64), tensors drawn
+in the listed order as float64 ``standard_normal``, weights multiplied by
+1/sqrt(d_model), then stored as float32 (fp32 workloads) or rounded to bf16
+with round-to-nearest-even (bf16 workloads).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "mha": projections + attention + W^O;  "attn": attention core only
+    dtype: str           # "f32" or "bf16": the stored type of every tensor
+    batch: int
+    heads: int
+    n_q: int
+    n_k: int
+    d_k: int
+    causal: bool
+    seed: int
+    d_model: int = 0     # mha workloads only
+    oracle_rows: int = 0  # >0: the oracle checks this many sampled query positions
+
+    @property
+    def d_v(self) -> int:
+        return self.d_k
+
+    def attention_pairs(self) -> int:
+        """Unmasked (query, key) pairs per (batch, head)."""
+        if self.causal:
+            return self.n_q * (self.n_q + 1) // 2
+        return self.n_q * self.n_k
+
+    def attention_flops(self) -> int:
+        """4 * B * H * d * pairs: QK^T and PV, two flops per multiply-add."""
+        return 4 * self.batch * self.heads * self.d_k * self.attention_pairs()
+
+    def projection_flops(self) -> int:
+        if self.kind != "mha":
+            return 0
+        dm = self.d_model
+        rows_q = self.batch * self.n_q
+        rows_k = self.batch * self.n_k
+        # Q, K, V projections and the output projection W^O
+        return 2 * dm * dm * (rows_q + 2 * rows_k + rows_q)
+
+    def total_flops(self) -> int:
+        return self.attention_flops() + self.projection_flops()
+
+
+WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("tiny_mha_f32_b1_n128", "mha", "f32", batch=1, heads=8, n_q=128,
+                 n_k=128, d_k=64, causal=False, seed=1, d_model=512),
+        Workload("base_encoder_mha_bf16_b32_n512", "mha", "bf16", batch=32, heads=8,
+                 n_q=512, n_k=512, d_k=64, causal=False, seed=2, d_model=512),
+        Workload("decoder_causal_bf16_b16_h8_n1024", "attn", "bf16", batch=16, heads=8,
+                 n_q=1024, n_k=1024, d_k=64, causal=True, seed=3),
+        Workload("cross_attn_bf16_b32_h8_nq384_nk512", "attn", "bf16", batch=32, heads=8,
+                 n_q=384, n_k=512, d_k=64, causal=False, seed=4),
+        Workload("long_causal_bf16_b2_h16_n8192", "attn", "bf16", batch=2, heads=16,
+                 n_q=8192, n_k=8192, d_k=64, causal=True, seed=5, oracle_rows=64),
+    ]
+}
+
+# Short aliases used by command-line flags.
+ALIASES = {
+    "tiny": "tiny_mha_f32_b1_n128",
+    "encoder": "base_encoder_mha_bf16_b32_n512",
+    "decoder": "decoder_causal_bf16_b16_h8_n1024",
+    "cross": "cross_attn_bf16_b32_h8_nq384_nk512",
+    "long": "long_causal_bf16_b2_h16_n8192",
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[ALIASES.get(name, name)]
+
+
+# ---------------------------------------------------------------- storage types
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (round to nearest, ties to even); return the raw uint16 bits.
+
+    The input is first stored as float32 (the recipe above), then the upper
+    16 bits are kept after adding the round-to-nearest-even bias. NaN does not
+    occur in these inputs.
+    """
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    bias = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bits to float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """x rounded to the nearest bf16 value, returned as float32."""
+    return bf16_bits_to_f32(bf16_bits(x))
+
+
+@dataclasses.dataclass
+class Stored:
+    """One stored tensor: its exact value (float64) and the bits the device gets."""
+    value: np.ndarray      # float64, exactly the stored value
+    dtype: str             # "f32" or "bf16"
+    raw: np.ndarray        # float32 array (f32) or uint16 bits (bf16), C-contiguous
+
+    @property
+    def shape(self):
+        return self.value.shape
+
+
+def store(x: np.ndarray, dtype: str) -> Stored:
+    if dtype == "f32":
+        f = np.ascontiguousarray(x, dtype=np.float32)
+        return Stored(f.astype(np.float64), "f32", f)
+    if dtype == "bf16":
+        bits = bf16_bits(x)
+        return Stored(bf16_bits_to_f32(bits).astype(np.float64), "bf16", bits)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------- generators
+
+def make_inputs(w: Workload, *, v_ones: bool = False) -> dict[str, Stored]:
+    """Draw the workload's tensors in the documented order.
+
+    mha:  x (B, N, d_model), then W^Q, W^K, W^V, W^O, each (d_model, d_model),
+          stored (in, out) so that Q = x @ W^Q. Self-attention: one x serves
+          as the query, key and value input.
+    attn: Q (B, H, N_q, d), K (B, H, N_k, d), V (B, H, N_k, d).
+    v_ones replaces V by all ones after drawing (row-sum checks); the draws
+    themselves are unchanged so Q and K stay identical to the plain run.
+    """
+    rng = np.random.default_rng(w.seed)
+    out: dict[str, Stored] = {}
+    if w.kind == "mha":
+        dm = w.d_model
+        out["x"] = store(rng.standard_normal((w.batch, w.n_q, dm)), w.dtype)
+        s = 1.0 / math.sqrt(dm)
+        for name in ("wq", "wk", "wv", "wo"):
+            out[name] = store(rng.standard_normal((dm, dm)) * s, w.dtype)
+        return out
+    out["q"] = store(rng.standard_normal((w.batch, w.heads, w.n_q, w.d_k)), w.dtype)
+    out["k"] = store(rng.standard_normal((w.batch, w.heads, w.n_k, w.d_k)), w.dtype)
+    v = rng.standard_normal((w.batch, w.heads, w.n_k, w.d_v))
+    if v_ones:
+        v = np.ones_like(v)
+    out["v"] = store(v, w.dtype)
+    return out
+
+
+def random_tensor(shape, dtype: str, seed: int, scale: float = 1.0) -> Stored:
+    """A seeded unit-normal tensor (times scale) for edge-shape tests."""
+    rng = np.random.default_rng(seed)
+    return store(rng.standard_normal(shape) * scale, dtype)
+
+
+# Fixed edge positions checked in every sampled run of the long causal workload:
+# the first rows, both sides of 64- and 128-row tile edges, the middle and the end.
+EDGE_ROWS = (0, 1, 63, 64, 127, 128, 4095, 4096, 8190, 8191)
+
+
+def sample_rows(w: Workload) -> np.ndarray:
+    """Query positions the oracle evaluates for a sampled workload, sorted."""
+    n = w.n_q
+    fixed = [r for r in EDGE_ROWS if r < n]
+    need = w.oracle_rows - len(fixed)
+    rng = np.random.default_rng(1000 + w.seed)
+    pool = np.setdiff1d(np.arange(n), np.array(fixed))
+    extra = rng.choice(pool, size=max(need, 0), replace=False)
+    return np.sort(np.concatenate([np.array(fixed, dtype=np.int64), extra.astype(np.int64)]))
