@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark: multi-head attention forward on one MI355X (gfx950).
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input.
+Default workload: the base-model encoder self-attention, bf16, batch 32,
+N = 512, d_model = 512, h = 8, d_k = 64, no mask; a step is one mha_forward
+(Q/K/V projections, attention, W^O). Attention-only workloads
+(--workload decoder|cross|long) time one attention_forward per step.
+
+Prints ONE JSON line. `value` is algorithmic TFLOP/s of the step (FLOPs =
+4*B*H*d*unmasked pairs for attention, 2*m*n*k per projection) with inputs
+already resident in HBM; input and output buffers rotate over more than twice
+the 256 MB Infinity Cache so each step reads its inputs from HBM.
+`roofline` covers the step's dominant kernel, timed with HIP events on the
+stream it runs on. `cpu_baseline` times the fp64 CPU oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+HBM_GBPS = 8000.0
+ROTATE_BYTES = 512 << 20    # > 2x the 256 MB Infinity Cache
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "attention": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_bf16.hip"),
+    "linear": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "linear_bf16.hip"),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def torch_tensor(stored, dev):
+    import torch
+    if stored.dtype == "bf16":
+        t = torch.from_numpy(stored.raw.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(stored.raw).copy())
+    return t.to(dev)
+
+
+def time_events(fn, iters, stream):
+    """Average milliseconds per call, HIP events on `stream` around `iters` calls."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(iters):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def traffic_for(kernel_key, launch_desc):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if that summary is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(launch_desc)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel_key]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, min_seconds=10.0, max_seconds=30.0):
+    """The fp64 oracle, untuned, on the host cores: repeat the sample until
+    ~min_seconds of CPU work; report algorithmic TFLOP/s of what it computed."""
+    import threadpoolctl
+    import oracle
+    info = threadpoolctl.threadpool_info()
+    threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    if w.kind == "mha":
+        xv = inputs["x"].value
+        args = (xv, xv, xv, inputs["wq"].value, inputs["wk"].value, inputs["wv"].value, inputs["wo"].value)
+        fn = lambda: oracle.mha_ref(*args, w.heads, causal=w.causal)
+        flops = w.total_flops()
+        sample = f"the full workload ({w.batch} batch elements), oracle.mha_ref in float64"
+    else:
+        rows = workloads.sample_rows(w) if w.oracle_rows else None
+        fn = lambda: oracle.attention_ref(inputs["q"].value, inputs["k"].value, inputs["v"].value,
+                                          causal=w.causal, rows=rows)
+        if rows is None:
+            flops = w.attention_flops()
+            sample = f"the full workload, oracle.attention_ref in float64"
+        else:
+            pairs = int(np.sum(rows + 1)) if w.causal else len(rows) * w.n_k
+            flops = 4 * w.batch * w.heads * w.d_k * pairs
+            sample = (f"{len(rows)} sampled query positions x {w.batch * w.heads} (batch, head) pairs, "
+                      "each against all visible keys, oracle.attention_ref in float64")
+    runs, t0 = 0, time.perf_counter()
+    result = None
+    while True:
+        result = fn()
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el + el / runs > max_seconds:
+            break
+    return {"value": round(flops * runs / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{sample}; {runs} run(s) in {el:.1f} s",
+            "host_cpus": os.cpu_count(), "blas": ",".join(sorted({d.get("internal_api", "?") for d in info}))}, result
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="encoder", help="encoder | tiny | decoder | cross | long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the long causal attention line")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is a design note, not an implemented path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_scaled_dot_mha_amd as mha
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mha.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    w = workloads.get(args.workload)
+    log(f"workload {w.name}: generating seeded inputs")
+    inputs = workloads.make_inputs(w)
+
+    result = {}
+    if w.kind == "mha":
+        dm = w.d_model
+        x = torch_tensor(inputs["x"], dev)
+        ws = [torch_tensor(inputs[n], dev) for n in ("wq", "wk", "wv", "wo")]
+        esz = x.element_size()
+        per_set = x.numel() * esz * 2
+        n_sets = max(1, math.ceil(ROTATE_BYTES / per_set))
+        xs = [x] + [x.clone() for _ in range(n_sets - 1)]
+        outs = [torch.empty_like(x) for _ in range(n_sets)]
+        need = mha.mha_forward_workspace_size(w.batch, w.n_q, w.n_k, dm, w.heads, x.dtype)
+        work = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def step(i):
+            xi = xs[i % n_sets]
+            mha.mha_forward(xi, xi, xi, *ws, w.heads, causal=w.causal, out=outs[i % n_sets], workspace=work)
+
+        # parity on the exact launch configuration that is timed
+        step(0)
+        torch.cuda.synchronize()
+        flops_step = w.total_flops()
+        # dominant kernel: the attention launch inside mha_forward, re-timed alone on the
+        # same workspace views (same kernel, same grid)
+        B, N, H, d = w.batch, w.n_q, w.heads, w.d_k
+        qv = work[:B * N * dm * esz].view(x.dtype).view(B, N, H, d).transpose(1, 2)
+        off_k = (B * N * dm * esz + 255) // 256 * 256
+        kv = work[off_k:off_k + B * w.n_k * dm * esz].view(x.dtype).view(B, w.n_k, H, d).transpose(1, 2)
+        off_v = off_k + (B * w.n_k * dm * esz + 255) // 256 * 256
+        vv = work[off_v:off_v + B * w.n_k * dm * esz].view(x.dtype).view(B, w.n_k, H, d).transpose(1, 2)
+        ov = torch.empty((B, N, H, d), dtype=x.dtype, device=dev).transpose(1, 2)
+        dom_fn = lambda i: mha.attention_forward(qv, kv, vv, causal=w.causal, out=ov)
+        dom_flops = w.attention_flops()
+        dom_name = "attn_fwd_bf16_d64" if w.dtype == "bf16" else "attn_fwd_f32"
+        dom_bytes = 2 * (B * H * N * d + 2 * B * H * w.n_k * d + B * H * N * d) * (esz // 2)
+        get_out = lambda: outs[0]
+    else:
+        q, k, v = (torch_tensor(inputs[n], dev) for n in ("q", "k", "v"))
+        per_set = (q.numel() + k.numel() + v.numel() + q.numel()) * q.element_size()
+        n_sets = max(1, math.ceil(ROTATE_BYTES / per_set))
+        sets = [(q, k, v)] + [(q.clone(), k.clone(), v.clone()) for _ in range(n_sets - 1)]
+        outs = [torch.empty_like(q) for _ in range(n_sets)]
+
+        def step(i):
+            qi, ki, vi = sets[i % n_sets]
+            mha.attention_forward(qi, ki, vi, causal=w.causal, out=outs[i % n_sets])
+
+        step(0)
+        torch.cuda.synchronize()
+        flops_step = w.attention_flops()
+        dom_fn, dom_flops, dom_name = step, flops_step, "attn_fwd_bf16_d64"
+        dom_bytes = per_set
+        get_out = lambda: outs[0]
+
+    log(f"warmup {args.warmup}, timing {args.steps} steps ({n_sets} rotating input sets)")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # single process on one GPU: the barrier is the device synchronisation itself
+    ms = time_events(step, args.steps, stream)
+    value = flops_step / (ms * 1e-3) / 1e12
+    log(f"step {ms * 1e3:.1f} us, {value:.1f} TFLOP/s")
+
+    dom_ms = time_events(dom_fn, max(args.steps, 20), stream)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    launch_desc = f"{dom_name}:{w.name}"
+    roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic_for("attention", launch_desc),
+                "algorithmic_bytes": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
+                "achieved_gbps": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1)}
+    log(f"dominant kernel {dom_name}: {dom_ms * 1e3:.1f} us, {achieved:.1f} TFLOP/s")
+
+    secondary = None
+    if not args.no_secondary and w.name != workloads.get("long").name:
+        wl = workloads.get("long")
+        xl = workloads.make_inputs(wl)
+        ql, kl, vl = (torch_tensor(xl[n], dev) for n in ("q", "k", "v"))
+        ol = torch.empty_like(ql)
+        fl = lambda i: mha.attention_forward(ql, kl, vl, causal=True, out=ol)
+        for i in range(3):
+            fl(i)
+        lms = time_events(fl, 20, stream)
+        lt = wl.attention_flops() / (lms * 1e-3) / 1e12
+        secondary = {"workload": wl.name, "kernel": "attn_fwd_bf16_d64", "us": round(lms * 1e3, 1),
+                     "tflops": round(lt, 1), "frac_of_peak": round(lt / PEAK_BF16_TFLOPS, 4)}
+        log(f"long causal attention: {lms * 1e3:.1f} us, {lt:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host cores")
+        cpu, ref = cpu_baseline(w, inputs)
+        got = get_out().float().cpu().numpy().astype(np.float64)
+        if w.kind == "attn" and w.oracle_rows:
+            got = got[:, :, workloads.sample_rows(w)]
+        ref_o = ref if w.kind == "mha" else ref[0]
+        err = float(np.max(np.abs(got - ref_o)))
+        result["parity_max_abs"] = err
+        log(f"parity vs oracle: max-abs {err:.3e}")
+
+    cfg = {"workload": w.name, "batch": w.batch, "seq_len_q": w.n_q, "seq_len_k": w.n_k, "heads": w.heads,
+           "d_k": w.d_k, "causal": w.causal,
+           "step": "mha_forward: QKV projections + attention + W^O" if w.kind == "mha" else "attention_forward"}
+    if w.kind == "mha":
+        cfg["d_model"] = w.d_model
+    line = {"metric": "attention fwd TFLOP/s and % of bf16 MFMA peak at 1 GPU (h=8, d_k=64)",
+            "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg,
+            "pct_of_peak": round(100 * value / peak, 2), "roofline": roofline, "cpu_baseline": cpu}
+    if secondary:
+        line["long_causal"] = secondary
+    line.update(result)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * mha.h -- C ABI of libmha.so: multi-head scaled dot-product attention,
+ * forward pass, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the pages' statement of the problem):
+ *   Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V, softmax over each row
+ *     -- "The Transformer" (hoshank.vercel.app), "The Mathematics", Attention
+ *     equation; "How Transformers Work" (worksonmygpu.com), "Scaled
+ *     dot-product attention".
+ *   MultiHead(Q, K, V) = Concat(head_1 .. head_h) W^O,
+ *   head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V)
+ *     -- same page, MultiHead equation; "32 Transformer"
+ *     (ml-canon-en.vercel.app), "PyTorch Implementation".
+ *   Causal mask: key j is blocked for query i when j > i (diagonal kept), by
+ *     adding -inf to the score before the softmax, so blocked keys weigh
+ *     exactly 0 -- "The Transformer" (rayaq.ca), "Masks: who may look at whom".
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is DEVICE memory owned by the caller. The library
+ *     never allocates, frees or retains device memory and keeps no state
+ *     between calls.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream). MHA_OK means "validated and enqueued"; faults during execution
+ *     surface at the caller's next synchronisation.
+ *   - All argument validation happens before any HIP runtime call, so invalid
+ *     arguments are reported without touching a device.
+ *   - No C++ exception crosses this boundary. On a non-OK status,
+ *     mha_last_error() returns a thread-local description.
+ *   - Element types: MHA_F32 = IEEE binary32; MHA_BF16 = bfloat16. In bf16
+ *     mode products accumulate in fp32, the softmax runs in fp32, the
+ *     attention weights are rounded to bf16 (nearest-even) for the P V
+ *     product, and every stored tensor (outputs and mha_forward's
+ *     intermediates) is rounded to bf16 (nearest-even).
+ *   - Output buffers must not overlap any input buffer.
+ */
+#ifndef MHA_H
+#define MHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mha_status {
+  MHA_OK = 0,
+  MHA_ERR_INVALID_ARG = 1, /* null pointer, size < 1, bad stride/alignment, causal with n_q != n_k, ... */
+  MHA_ERR_UNSUPPORTED = 2, /* valid request outside what this build implements (e.g. d_k != 64 in bf16) */
+  MHA_ERR_WORKSPACE = 3,   /* workspace smaller than mha_forward_workspace_size() */
+  MHA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} mha_status;
+
+typedef enum mha_dtype { MHA_F32 = 0, MHA_BF16 = 1 } mha_dtype;
+
+/*
+ * attention_forward -- scaled dot-product attention for every (batch, head).
+ *
+ *   O[b,h,i,:] = sum_j P[b,h,i,j] V[b,h,j,:],
+ *   P[b,h,i,:] = softmax_j( scale * Q[b,h,i,:] . K[b,h,j,:]  (+ causal mask) )
+ *
+ * q: (batch, heads, n_q, d_k)   k: (batch, heads, n_k, d_k)
+ * v: (batch, heads, n_k, d_v)   o: (batch, heads, n_q, d_v)   all of `dtype`
+ *   Each tensor is addressed through its own element strides
+ *   {batch, head, row}; the last dimension is contiguous (stride 1). So the
+ *   head split and concat of multi-head attention are pure stride choices:
+ *   a (batch, n, heads*d) buffer is passed with strides {n*heads*d, d, heads*d}.
+ * causal: 0 = no mask (encoder self-attention, cross-attention);
+ *   1 = key j blocked for query i when j > i (requires n_q == n_k).
+ * scale: multiplies the scores before the softmax; 1/sqrt(d_k) gives the
+ *   pages' attention, other values act as an inverse temperature ("The
+ *   Transformer" (rayaq.ca), "Worked example"). Must be finite; 0 gives
+ *   uniform weights over the visible keys.
+ * lse: NULL, or fp32 (batch, heads, n_q) contiguous: on return
+ *   lse[b,h,i] = log sum_j exp(scale * q_i . k_j) over the visible keys.
+ *
+ * Supported in this build: d_k == d_v; bf16 needs d_k == 64 (both page model
+ *   sizes use 64); f32 accepts d_k in {16, 32, 64, 128}. Otherwise
+ *   MHA_ERR_UNSUPPORTED.
+ * Alignment: base pointers 16-byte aligned; every stride a multiple of
+ *   8 elements (bf16) or 4 elements (f32). Otherwise MHA_ERR_INVALID_ARG.
+ */
+mha_status attention_forward(const void* q, const void* k, const void* v, void* o,
+                             int batch, int heads, int n_q, int n_k, int d_k, int d_v,
+                             const int64_t q_strides[3], const int64_t k_strides[3],
+                             const int64_t v_strides[3], const int64_t o_strides[3],
+                             mha_dtype dtype, int causal, float scale, float* lse,
+                             void* stream);
+
+/*
+ * linear_forward -- one projection, Y = X W (no bias), the building block of
+ * the Q/K/V projections and of W^O ("The Transformer" (hoshank.vercel.app),
+ * "The Mathematics": W_i^Q etc. are d_model x d_k matrices applied on the
+ * right; "32 Transformer", "PyTorch Implementation": Q = x @ Wq).
+ *
+ * x: (m, k) row-major with leading dimension ldx; w: (k, n) row-major (in, out)
+ * with leading dimension ldw; y: (m, n) row-major with leading dimension ldy.
+ * fp32 accumulation; y rounded to `dtype`.
+ * Alignment: base pointers 16-byte aligned; k, n and the leading dimensions
+ *   multiples of 8 (bf16) or 4 (f32); otherwise MHA_ERR_INVALID_ARG.
+ */
+mha_status linear_forward(const void* x, const void* w, void* y, int m, int n, int k,
+                          int64_t ldx, int64_t ldw, int64_t ldy, mha_dtype dtype, void* stream);
+
+/*
+ * mha_forward_workspace_size -- bytes of device workspace mha_forward needs:
+ * room for the projected Q (batch*n_q x d_model), K and V (batch*n_k x
+ * d_model each) and the concatenated head outputs (batch*n_q x d_model), in
+ * `dtype`, each region 256-byte aligned. Returns 0 for invalid sizes.
+ */
+size_t mha_forward_workspace_size(int batch, int n_q, int n_k, int d_model, int heads,
+                                  mha_dtype dtype);
+
+/*
+ * mha_forward -- multi-head attention, bias-free:
+ *   out = Concat_i( Attention(Xq W^Q_i, Xk W^K_i, Xv W^V_i) ) W^O,
+ *   scale 1/sqrt(d_model / heads); head i owns columns [i*d, (i+1)*d) of each
+ *   projection and rows [i*d, (i+1)*d) of W^O.
+ *
+ * xq: (batch, n_q, d_model); xk, xv: (batch, n_k, d_model), all contiguous.
+ *   Self-attention passes the same pointer three times; encoder-decoder
+ *   cross-attention passes the decoder state as xq and the encoder memory as
+ *   xk and xv ("The Transformer" (rayaq.ca), "The decoder stack").
+ * wq, wk, wv, wo: (d_model, d_model) row-major, stored (in, out) so Q = X W^Q.
+ * out: (batch, n_q, d_model).
+ * workspace: device memory of at least mha_forward_workspace_size() bytes,
+ *   16-byte aligned, owned by the caller; its contents are scratch (the
+ *   projected Q, K, V and the concatenated heads are left there on return).
+ * causal: as in attention_forward (requires n_q == n_k).
+ * d_model % heads must be 0 (MHA_ERR_INVALID_ARG otherwise); the head width
+ *   d_model/heads follows attention_forward's support rules.
+ * Launches: one grouped projection for Q, K and V, one attention, one W^O
+ *   projection, all on `stream`.
+ */
+mha_status mha_forward(const void* xq, const void* xk, const void* xv, const void* wq,
+                       const void* wk, const void* wv, const void* wo, void* out,
+                       void* workspace, size_t workspace_bytes, int batch, int n_q, int n_k,
+                       int d_model, int heads, mha_dtype dtype, int causal, void* stream);
+
+/* Static English name of a status code (never NULL). */
+const char* mha_status_string(mha_status status);
+
+/* Thread-local detail text for the most recent non-OK status returned on the
+ * calling thread ("" if none). Valid until the next call on this thread. */
+const char* mha_last_error(void);
+
+/* ABI version of this library: major * 10000 + minor * 100 + patch. */
+int mha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_H */

@@ -183,3 +183,10 @@ def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: 
     o, _, _ = attention_ref(qh, kh, vh, causal=causal, scale=1.0 / math.sqrt(d_model // heads),
                             rows=rows)
     return np.matmul(concat_heads(o), np.asarray(wo, dtype=np.float64))
+
+
+def linear_ref(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """One projection Y = X W (no bias), the per-head projection of the
+    MultiHead equation ("The Transformer" (hoshank.vercel.app), "The
+    Mathematics"), in float64."""
+    return np.matmul(np.asarray(x, dtype=np.float64), np.asarray(w, dtype=np.float64))

@@ -57,3 +57,18 @@ def test_causal_rejects_cross_shapes():
     q, k = r.standard_normal((1, 1, 3, 2)), r.standard_normal((1, 1, 5, 2))
     with pytest.raises(ValueError):
         oracle.attention_ref(q, k, k, causal=True)
+
+
+def test_linear_is_the_projection_used_by_mha():
+    # h = 1 with W^O = I: mha output = attention over the three projections
+    r = np.random.default_rng(5)
+    x = r.standard_normal((2, 4, 6))
+    wq, wk, wv = (r.standard_normal((6, 6)) for _ in range(3))
+    out = oracle.mha_ref(x, x, x, wq, wk, wv, np.eye(6), 1)
+    q, k, v = (oracle.linear_ref(x, w)[:, None] for w in (wq, wk, wv))
+    o, _, _ = oracle.attention_ref(q, k, v)
+    assert np.allclose(out, o[:, 0], rtol=0, atol=1e-12)
+    # and it is the row-by-column product: entry (i, j) = sum_t x[i, t] w[t, j]
+    a, b = r.standard_normal((3, 5)), r.standard_normal((5, 2))
+    y = oracle.linear_ref(a, b)
+    assert abs(y[2, 1] - sum(a[2, t] * b[t, 1] for t in range(5))) < 1e-13

@@ -1,0 +1,267 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs (GPU).
+
+Bars: max-abs error <= 1e-4 (fp32) or <= 2e-2 (bf16) on unit-variance inputs;
+softmax row sums within 1e-3 of 1. Everything is called through the C ABI
+(via the thin binding). Sizes: every workload at its full size (the long
+causal one checked on sampled query positions, all keys each), plus small
+ragged shapes that span several tiles and a partial tail.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import transformer_scaled_dot_mha_amd as mha
+import workloads
+from tests.gpu_util import LSE_TOL, ROWSUM_TOL, TOL, assert_close, device, max_abs, say, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _attn_inputs(w, dev, v_ones=False):
+    x = workloads.make_inputs(w, v_ones=v_ones)
+    return x, to_device(x["q"], dev), to_device(x["k"], dev), to_device(x["v"], dev)
+
+
+def _oracle_rows(w):
+    return workloads.sample_rows(w) if w.oracle_rows else None
+
+
+# ---------------------------------------------------------------- the five workloads
+@pytest.mark.parametrize("name", ["decoder", "cross", "long"])
+def test_attention_workload_parity(dev, name):
+    import torch
+    w = workloads.get(name)
+    x, q, k, v = _attn_inputs(w, dev)
+    say(f"attention_forward {w.name}")
+    o, lse = mha.attention_forward(q, k, v, causal=w.causal, return_lse=True)
+    torch.cuda.synchronize()
+    rows = _oracle_rows(w)
+    want, _, want_lse = oracle.attention_ref(x["q"].value, x["k"].value, x["v"].value, causal=w.causal,
+                                             rows=rows)
+    got = to_f64(o) if rows is None else to_f64(o[:, :, torch.as_tensor(rows, device=dev)])
+    got_lse = to_f64(lse) if rows is None else to_f64(lse[:, :, torch.as_tensor(rows, device=dev)])
+    err = assert_close(got, want, w.dtype, w.name)
+    assert max_abs(got_lse, want_lse) <= LSE_TOL[w.dtype], "log-sum-exp"
+    say(f"{w.name}: max-abs {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "encoder"])
+def test_mha_workload_parity(dev, name):
+    import torch
+    w = workloads.get(name)
+    x = workloads.make_inputs(w)
+    t = {k_: to_device(s, dev) for k_, s in x.items()}
+    say(f"mha_forward {w.name}")
+    out = mha.mha_forward(t["x"], t["x"], t["x"], t["wq"], t["wk"], t["wv"], t["wo"], w.heads)
+    torch.cuda.synchronize()
+    xv = x["x"].value
+    want = oracle.mha_ref(xv, xv, xv, x["wq"].value, x["wk"].value, x["wv"].value, x["wo"].value, w.heads)
+    err = assert_close(to_f64(out), want, w.dtype, w.name)
+    say(f"{w.name}: max-abs {err:.3e}")
+
+
+# ---------------------------------------------------------------- row sums
+@pytest.mark.parametrize("name", ["decoder", "cross", "long"])
+def test_row_sums_with_v_ones(dev, name):
+    """With V = 1 every output element is the row sum of the weights."""
+    import torch
+    w = workloads.get(name)
+    _, q, k, v = _attn_inputs(w, dev, v_ones=True)
+    say(f"row sums {w.name}")
+    o = mha.attention_forward(q, k, v, causal=w.causal)
+    torch.cuda.synchronize()
+    dev_err = float((o.float() - 1.0).abs().max())
+    assert dev_err <= ROWSUM_TOL, f"row sum off by {dev_err}"
+
+
+def test_lse_normalises_the_scores(dev):
+    """sum_j exp(scale q_i.k_j - lse_i), evaluated on the host in fp64, is 1 to
+    within the normaliser's bf16 rounding bound (exp(LSE_TOL) - 1)."""
+    import torch
+    w = workloads.get("long")
+    x, q, k, v = _attn_inputs(w, dev)
+    _, lse = mha.attention_forward(q, k, v, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    rows = workloads.sample_rows(w)[::4]
+    lse_h = to_f64(lse)
+    qv, kv = x["q"].value, x["k"].value
+    for b in range(w.batch):
+        for h in (0, w.heads - 1):
+            s = qv[b, h, rows] @ kv[b, h].T * 0.125
+            s = np.where(np.arange(w.n_k)[None, :] > rows[:, None], -np.inf, s)
+            tot = np.exp(s - lse_h[b, h, rows][:, None]).sum(-1)
+            assert np.max(np.abs(tot - 1.0)) <= math.expm1(LSE_TOL["bf16"])
+
+
+# ---------------------------------------------------------------- edge shapes
+EDGE = [
+    # (B, H, n_q, n_k, causal, dtype)
+    (1, 1, 1, 1, False, "bf16"),
+    (1, 1, 1, 1, True, "bf16"),
+    (1, 2, 63, 63, True, "bf16"),
+    (2, 1, 65, 65, True, "bf16"),
+    (1, 3, 129, 129, False, "bf16"),
+    (1, 1, 1000, 1000, True, "bf16"),
+    (2, 2, 200, 77, False, "bf16"),
+    (1, 2, 5, 300, False, "bf16"),
+    (1, 1, 257, 1, False, "bf16"),
+    (1, 1, 1, 1, True, "f32"),
+    (2, 3, 65, 65, True, "f32"),
+    (1, 2, 100, 37, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,H,nq,nk,causal,dtype", EDGE)
+def test_edge_shapes(dev, B, H, nq, nk, causal, dtype):
+    import torch
+    d = 64
+    q = workloads.random_tensor((B, H, nq, d), dtype, seed=100 + nq)
+    k = workloads.random_tensor((B, H, nk, d), dtype, seed=200 + nk)
+    v = workloads.random_tensor((B, H, nk, d), dtype, seed=300 + nk)
+    say(f"edge {B}x{H} nq={nq} nk={nk} causal={causal} {dtype}")
+    o = mha.attention_forward(to_device(q, dev), to_device(k, dev), to_device(v, dev), causal=causal)
+    torch.cuda.synchronize()
+    want, _, _ = oracle.attention_ref(q.value, k.value, v.value, causal=causal)
+    assert_close(to_f64(o), want, dtype, "edge")
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_f32_head_widths(dev, d):
+    import torch
+    q = workloads.random_tensor((2, 2, 70, d), "f32", seed=400 + d)
+    k = workloads.random_tensor((2, 2, 70, d), "f32", seed=500 + d)
+    v = workloads.random_tensor((2, 2, 70, d), "f32", seed=600 + d)
+    for causal in (False, True):
+        say(f"f32 d={d} causal={causal}")
+        o = mha.attention_forward(to_device(q, dev), to_device(k, dev), to_device(v, dev), causal=causal)
+        torch.cuda.synchronize()
+        want, _, _ = oracle.attention_ref(q.value, k.value, v.value, causal=causal)
+        assert_close(to_f64(o), want, "f32", f"f32 d={d}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_head_views(dev, dtype):
+    """(B, N, H, d) buffers used through transposed views: the head split as strides."""
+    import torch
+    B, N, H, d = 2, 150, 4, 64
+    qs = workloads.random_tensor((B, N, H, d), dtype, seed=7)
+    ks = workloads.random_tensor((B, N, H, d), dtype, seed=8)
+    vs = workloads.random_tensor((B, N, H, d), dtype, seed=9)
+    q, k, v = (to_device(s, dev).transpose(1, 2) for s in (qs, ks, vs))
+    out = torch.zeros((B, N, H, d), dtype=q.dtype, device=dev)
+    say(f"strided views {dtype}")
+    mha.attention_forward(q, k, v, causal=True, out=out.transpose(1, 2))
+    torch.cuda.synchronize()
+    t = lambda s: s.value.transpose(0, 2, 1, 3)
+    want, _, _ = oracle.attention_ref(t(qs), t(ks), t(vs), causal=True)
+    assert_close(to_f64(out).transpose(0, 2, 1, 3), want, dtype, "strided")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.3, 2.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scale_values(dev, scale, dtype):
+    """Scale acts as an inverse temperature; 0 gives uniform weights, negative flips the order."""
+    import torch
+    q = workloads.random_tensor((1, 2, 130, 64), dtype, seed=11)
+    k = workloads.random_tensor((1, 2, 130, 64), dtype, seed=12)
+    v = workloads.random_tensor((1, 2, 130, 64), dtype, seed=13)
+    for causal in (False, True):
+        say(f"scale={scale} {dtype} causal={causal}")
+        o = mha.attention_forward(to_device(q, dev), to_device(k, dev), to_device(v, dev), causal=causal,
+                                  scale=scale)
+        torch.cuda.synchronize()
+        want, _, _ = oracle.attention_ref(q.value, k.value, v.value, causal=causal, scale=scale)
+        assert_close(to_f64(o), want, dtype, f"scale {scale}")
+
+
+# ---------------------------------------------------------------- properties on GPU outputs
+def test_deterministic(dev):
+    import torch
+    w = workloads.get("decoder")
+    _, q, k, v = _attn_inputs(w, dev)
+    say("determinism")
+    a = mha.attention_forward(q, k, v, causal=True)
+    b = mha.attention_forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_causal_locality_on_gpu(dev):
+    """Changing rows > i of Q, K, V leaves GPU output rows <= i bitwise unchanged."""
+    import torch
+    q = workloads.random_tensor((1, 2, 300, 64), "bf16", seed=21)
+    k = workloads.random_tensor((1, 2, 300, 64), "bf16", seed=22)
+    v = workloads.random_tensor((1, 2, 300, 64), "bf16", seed=23)
+    tq, tk, tv = (to_device(s, dev) for s in (q, k, v))
+    o = mha.attention_forward(tq, tk, tv, causal=True)
+    for i in (0, 63, 64, 200):
+        q2, k2, v2 = tq.clone(), tk.clone(), tv.clone()
+        for t in (q2, k2, v2):
+            t[:, :, i + 1:] = -t[:, :, i + 1:] * 2
+        say(f"causal locality i={i}")
+        o2 = mha.attention_forward(q2, k2, v2, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o2[:, :, :i + 1], o[:, :, :i + 1])
+
+
+def test_key_permutation_invariance_on_gpu(dev):
+    import torch
+    w = workloads.get("cross")
+    _, q, k, v = _attn_inputs(w, dev)
+    perm = torch.as_tensor(np.random.default_rng(5).permutation(w.n_k), device=dev)
+    say("key permutation")
+    a = mha.attention_forward(q, k, v)
+    b = mha.attention_forward(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous())
+    torch.cuda.synchronize()
+    assert float((a.float() - b.float()).abs().max()) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- projections and full MHA variants
+@pytest.mark.parametrize("m,n,k,dtype", [(1, 8, 8, "bf16"), (300, 136, 72, "bf16"), (2048, 512, 512, "bf16"),
+                                         (37, 20, 12, "f32"), (129, 512, 512, "f32")])
+def test_linear_parity(dev, m, n, k, dtype):
+    import torch
+    x = workloads.random_tensor((m, k), dtype, seed=31)
+    wt = workloads.random_tensor((k, n), dtype, seed=32, scale=1 / math.sqrt(k))
+    say(f"linear {m}x{k}x{n} {dtype}")
+    y = mha.linear_forward(to_device(x, dev), to_device(wt, dev))
+    torch.cuda.synchronize()
+    assert_close(to_f64(y), oracle.linear_ref(x.value, wt.value), dtype, "linear")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mha_cross_and_causal(dev, dtype):
+    import torch
+    B, nq, nk, dm, h = 2, 70, 130, 256 if dtype == "f32" else 512, 8 if dtype == "bf16" else 4
+    xq = workloads.random_tensor((B, nq, dm), dtype, seed=41)
+    mem = workloads.random_tensor((B, nk, dm), dtype, seed=42)
+    ws = [workloads.random_tensor((dm, dm), dtype, seed=43 + i, scale=1 / math.sqrt(dm)) for i in range(4)]
+    tw = [to_device(s, dev) for s in ws]
+    say(f"mha cross {dtype}")
+    out = mha.mha_forward(to_device(xq, dev), to_device(mem, dev), to_device(mem, dev), *tw, h)
+    torch.cuda.synchronize()
+    want = oracle.mha_ref(xq.value, mem.value, mem.value, *[s.value for s in ws], h)
+    assert_close(to_f64(out), want, dtype, "mha cross")
+    say(f"mha causal {dtype}")
+    xs = workloads.random_tensor((B, nk, dm), dtype, seed=47)
+    t = to_device(xs, dev)
+    out = mha.mha_forward(t, t, t, *tw, h, causal=True)
+    torch.cuda.synchronize()
+    want = oracle.mha_ref(xs.value, xs.value, xs.value, *[s.value for s in ws], h, causal=True)
+    assert_close(to_f64(out), want, dtype, "mha causal")
+
+
+def test_binding_reports_workspace_error(dev):
+    import torch
+    w = workloads.get("tiny")
+    x = {k_: to_device(s, dev) for k_, s in workloads.make_inputs(w).items()}
+    small = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(mha.MHAError, match="MHA_ERR_WORKSPACE"):
+        mha.mha_forward(x["x"], x["x"], x["x"], x["wq"], x["wk"], x["wv"], x["wo"], 8, workspace=small)

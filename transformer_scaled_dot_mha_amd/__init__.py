@@ -1,0 +1,153 @@
+"""Multi-head scaled dot-product attention forward for AMD MI355X (gfx950).
+
+Thin Python binding over libmha.so's C ABI (include/mha.h): each function
+checks and marshals torch tensors (device pointers, element strides, the
+current HIP stream) and calls the C entry point of the same name. Every step
+of the computation runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback, and calling with CPU tensors raises.
+"""
+from __future__ import annotations
+
+import math
+
+from ._lib import (MHA_BF16, MHA_ERR_HIP, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED,
+                   MHA_ERR_WORKSPACE, MHA_F32, MHA_OK, LIB_PATH, MHAError, check, load, strides3)
+
+__all__ = ["attention_forward", "linear_forward", "mha_forward", "mha_forward_workspace_size",
+           "MHAError", "MHA_F32", "MHA_BF16", "LIB_PATH", "load"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MHA_F32
+    if t.dtype == torch.bfloat16:
+        return MHA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.float32 or torch.bfloat16")
+
+
+def _require_device(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (no CPU path exists)")
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if t.dtype != ts[0].dtype:
+            raise TypeError("all tensors must share one dtype")
+    return dev
+
+
+def _stream_handle(dev, stream):
+    torch = _torch()
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    return s.cuda_stream
+
+
+def attention_forward(q, k, v, *, causal: bool = False, scale: float | None = None, out=None,
+                      return_lse: bool = False, stream=None):
+    """O = softmax(scale * Q K^T (+ causal mask)) V for (batch, heads, n, d) tensors.
+
+    q: (B, H, N_q, d), k: (B, H, N_k, d), v: (B, H, N_k, d); any strides with a
+    contiguous last dimension (so (B, N, H, d) buffers can be passed through
+    .transpose(1, 2) without a copy). Returns out (B, H, N_q, d), and the fp32
+    log-sum-exp (B, H, N_q) when return_lse is set.
+    """
+    torch = _torch()
+    dev = _require_device(q, k, v)
+    B, H, n_q, d_k = q.shape
+    n_k, d_v = k.shape[2], v.shape[3]
+    if k.shape[:2] != (B, H) or v.shape[:3] != (B, H, n_k) or k.shape[3] != d_k:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+    if out is None:
+        out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=dev)
+    _require_device(q, out)
+    if tuple(out.shape) != (B, H, n_q, d_v) or out.stride(3) != 1:
+        raise ValueError("out must be (B, H, N_q, d_v) with a contiguous last dimension")
+    lse = torch.empty((B, H, n_q), dtype=torch.float32, device=dev) if return_lse else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    lib = load()
+    with torch.cuda.device(dev):
+        st = lib.attention_forward(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, n_q, n_k, d_k, d_v,
+            strides3(q.stride()[:3]), strides3(k.stride()[:3]), strides3(v.stride()[:3]),
+            strides3(out.stride()[:3]), _dtype_code(q), int(bool(causal)), float(scale),
+            lse.data_ptr() if lse is not None else None, _stream_handle(dev, stream))
+    check(st)
+    return (out, lse) if return_lse else out
+
+
+def linear_forward(x, w, *, out=None, stream=None):
+    """Y = X W for X (m, k) and W (k, n) row-major (leading dimension = row stride)."""
+    torch = _torch()
+    dev = _require_device(x, w)
+    m, k = x.shape
+    k2, n = w.shape
+    if k2 != k:
+        raise ValueError(f"inner sizes differ: {k} vs {k2}")
+    if x.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("x and w must be row-major with contiguous rows")
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=dev)
+    _require_device(x, out)
+    if tuple(out.shape) != (m, n) or out.stride(1) != 1:
+        raise ValueError("out must be (m, n) row-major")
+    lib = load()
+    with torch.cuda.device(dev):
+        st = lib.linear_forward(x.data_ptr(), w.data_ptr(), out.data_ptr(), m, n, k, x.stride(0),
+                                w.stride(0), out.stride(0), _dtype_code(x), _stream_handle(dev, stream))
+    check(st)
+    return out
+
+
+def mha_forward_workspace_size(batch: int, n_q: int, n_k: int, d_model: int, heads: int, dtype) -> int:
+    """Bytes of workspace mha_forward needs (dtype: torch dtype or MHA_F32/MHA_BF16)."""
+    code = dtype if isinstance(dtype, int) else (MHA_BF16 if str(dtype).endswith("bfloat16") else MHA_F32)
+    return int(load().mha_forward_workspace_size(batch, n_q, n_k, d_model, heads, code))
+
+
+def mha_forward(xq, xk, xv, wq, wk, wv, wo, heads: int, *, causal: bool = False, out=None,
+                workspace=None, stream=None):
+    """MultiHead(xq, xk, xv) = Concat(head_1..head_h) W^O, bias-free.
+
+    xq (B, N_q, d_model); xk, xv (B, N_k, d_model); w* (d_model, d_model) stored
+    (in, out). Pass the same tensor three times for self-attention. workspace,
+    if given, is a uint8 device tensor of at least mha_forward_workspace_size bytes.
+    """
+    torch = _torch()
+    dev = _require_device(xq, xk, xv, wq, wk, wv, wo)
+    B, n_q, d_model = xq.shape
+    n_k = xk.shape[1]
+    if xk.shape != (B, n_k, d_model) or xv.shape != xk.shape:
+        raise ValueError("xk and xv must be (B, N_k, d_model)")
+    for w in (wq, wk, wv, wo):
+        if tuple(w.shape) != (d_model, d_model):
+            raise ValueError("weights must be (d_model, d_model)")
+    for t in (xq, xk, xv, wq, wk, wv, wo):
+        if not t.is_contiguous():
+            raise ValueError("mha_forward takes contiguous tensors")
+    code = _dtype_code(xq)
+    lib = load()
+    need = int(lib.mha_forward_workspace_size(B, n_q, n_k, d_model, heads, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((B, n_q, d_model), dtype=xq.dtype, device=dev)
+    if tuple(out.shape) != (B, n_q, d_model) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B, N_q, d_model) tensor")
+    with torch.cuda.device(dev):
+        st = lib.mha_forward(xq.data_ptr(), xk.data_ptr(), xv.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+                             wv.data_ptr(), wo.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), B, n_q, n_k, d_model, heads,
+                             code, int(bool(causal)), _stream_handle(dev, stream))
+    check(st)
+    return out

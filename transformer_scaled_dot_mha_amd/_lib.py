@@ -1,0 +1,76 @@
+"""ctypes loader for libmha.so (built in-tree by build.py).
+
+This module imports nothing but the standard library, so the C ABI can be
+loaded and inspected on a machine without a GPU. There is no fallback: if the
+library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
+
+MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_WORKSPACE, MHA_ERR_HIP = range(5)
+MHA_F32, MHA_BF16 = 0, 1
+
+_i64x3 = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+_int = ctypes.c_int
+
+# name -> (restype, argtypes); must match include/mha.h
+SIGNATURES = {
+    "attention_forward": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int,
+                                 _i64x3, _i64x3, _i64x3, _i64x3, _int, _int, ctypes.c_float,
+                                 _vp, _vp]),
+    "linear_forward": (_int, [_vp, _vp, _vp, _int, _int, _int, ctypes.c_int64, ctypes.c_int64,
+                              ctypes.c_int64, _int, _vp]),
+    "mha_forward_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int, _int, _int]),
+    "mha_forward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                           _int, _int, _int, _int, _int, _int, _int, _vp]),
+    "mha_status_string": (ctypes.c_char_p, [_int]),
+    "mha_last_error": (ctypes.c_char_p, []),
+    "mha_version": (_int, []),
+}
+
+
+class MHAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{_status_name(status)}: {detail}")
+
+
+_lib = None
+
+
+def _status_name(status: int) -> str:
+    names = ["MHA_OK", "MHA_ERR_INVALID_ARG", "MHA_ERR_UNSUPPORTED", "MHA_ERR_WORKSPACE", "MHA_ERR_HIP"]
+    return names[status] if 0 <= status < len(names) else f"status {status}"
+
+
+def load() -> ctypes.CDLL:
+    """Load libmha.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m transformer_scaled_dot_mha_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def strides3(s) -> ctypes.Array:
+    return (ctypes.c_int64 * 3)(*[int(x) for x in s])
+
+
+def check(status: int) -> None:
+    if status != MHA_OK:
+        raise MHAError(status, load().mha_last_error().decode())

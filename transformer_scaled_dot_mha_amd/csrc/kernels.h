@@ -1,0 +1,46 @@
+// Internal launchers between the C-ABI front end and the HIP kernels.
+// Arguments arrive here already validated; each launcher only enqueues.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mha {
+
+// One attention problem over all (batch, head) pairs. Strides in elements.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // nullable, (batch, heads, n_q) contiguous
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int batch, heads, n_q, n_k, d;
+  int causal;
+  float scale;
+};
+
+// Up to three independent projections Y_g = X_g W_g sharing n and k, done in
+// one launch (the grid's z index selects the group).
+struct LinearGroup {
+  const void* x;
+  const void* w;
+  void* y;
+  int m;
+  int64_t ldx, ldw, ldy;
+};
+struct LinearArgs {
+  LinearGroup g[3];
+  int groups;
+  int n, k;
+};
+
+hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream);
+hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream);
+
+}  // namespace mha

@@ -1,0 +1,290 @@
+// C-ABI front end of libmha.so: argument validation, workspace layout,
+// kernel dispatch, status codes and thread-local error text.
+//
+// Every check runs before the first HIP runtime call, so a bad argument is
+// reported on a machine without a GPU. No C++ exception leaves this file.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kernels.h"
+#include "mha.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mha_status fail(mha_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mha_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MHA_OK;
+  return fail(MHA_ERR_HIP, "%s: %s (hip error %d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Element multiple that keeps every 16-byte vector access aligned.
+int vec_elems(mha_dtype t) { return t == MHA_BF16 ? 8 : 4; }
+size_t elem_bytes(mha_dtype t) { return t == MHA_BF16 ? 2 : 4; }
+bool valid_dtype(int t) { return t == MHA_F32 || t == MHA_BF16; }
+bool f32_head_width(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace regions of mha_forward: Q, K, V, concatenated heads.
+struct WsLayout {
+  size_t q, k, v, o, total;
+};
+
+bool ws_layout(int batch, int n_q, int n_k, int d_model, mha_dtype t, WsLayout* w) {
+  const unsigned __int128 e = elem_bytes(t);
+  const unsigned __int128 rq = (unsigned __int128)batch * n_q * d_model * e;
+  const unsigned __int128 rk = (unsigned __int128)batch * n_k * d_model * e;
+  const unsigned __int128 tot = 2 * (rq + kAlign) + 2 * (rk + kAlign);
+  if (tot > ((unsigned __int128)1 << 62)) return false;
+  w->q = 0;
+  w->k = round_up((size_t)rq);
+  w->v = w->k + round_up((size_t)rk);
+  w->o = w->v + round_up((size_t)rk);
+  w->total = w->o + round_up((size_t)rq);
+  return true;
+}
+
+mha_status check_head_width(mha_dtype dtype, int d_k, int d_v) {
+  if (d_k != d_v) return fail(MHA_ERR_UNSUPPORTED, "d_k (%d) != d_v (%d) is not supported", d_k, d_v);
+  if (dtype == MHA_BF16 && d_k != 64)
+    return fail(MHA_ERR_UNSUPPORTED, "bf16 attention supports d_k = 64 only (got %d)", d_k);
+  if (dtype == MHA_F32 && !f32_head_width(d_k))
+    return fail(MHA_ERR_UNSUPPORTED, "f32 attention supports d_k in {16, 32, 64, 128} (got %d)", d_k);
+  return MHA_OK;
+}
+
+mha_status validate_attention(const void* q, const void* k, const void* v, void* o, int batch,
+                              int heads, int n_q, int n_k, int d_k, int d_v, const int64_t* qs,
+                              const int64_t* ks, const int64_t* vs, const int64_t* os, int dtype,
+                              int causal, float scale) {
+  if (!q || !k || !v || !o) return fail(MHA_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  if (!qs || !ks || !vs || !os) return fail(MHA_ERR_INVALID_ARG, "stride arrays must be non-null");
+  if (batch < 1 || heads < 1 || n_q < 1 || n_k < 1 || d_k < 1 || d_v < 1)
+    return fail(MHA_ERR_INVALID_ARG, "sizes must be >= 1 (batch=%d heads=%d n_q=%d n_k=%d d_k=%d d_v=%d)",
+                batch, heads, n_q, n_k, d_k, d_v);
+  if (!valid_dtype(dtype)) return fail(MHA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (causal && n_q != n_k)
+    return fail(MHA_ERR_INVALID_ARG, "the causal mask is defined for n_q == n_k (got %d and %d)", n_q, n_k);
+  if (!isfinite(scale)) return fail(MHA_ERR_INVALID_ARG, "scale must be finite");
+  mha_status s = check_head_width((mha_dtype)dtype, d_k, d_v);
+  if (s != MHA_OK) return s;
+  const int vec = vec_elems((mha_dtype)dtype);
+  const void* ptrs[4] = {q, k, v, o};
+  const char* names[4] = {"q", "k", "v", "o"};
+  const int64_t* strides[4] = {qs, ks, vs, os};
+  for (int t = 0; t < 4; ++t) {
+    if (!aligned16(ptrs[t])) return fail(MHA_ERR_INVALID_ARG, "%s must be 16-byte aligned", names[t]);
+    for (int i = 0; i < 3; ++i) {
+      if (strides[t][i] < 0) return fail(MHA_ERR_INVALID_ARG, "%s stride %d is negative", names[t], i);
+      if (strides[t][i] % vec)
+        return fail(MHA_ERR_INVALID_ARG, "%s stride %d (%lld) must be a multiple of %d elements", names[t],
+                    i, (long long)strides[t][i], vec);
+    }
+  }
+  // grid: one workgroup per (batch, head, 64- or 128-row query block)
+  const int64_t blocks = (int64_t)batch * heads * ((n_q + 63) / 64);
+  if (blocks > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "too many (batch, head, query block) triples");
+  return MHA_OK;
+}
+
+mha::AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                        int heads, int n_q, int n_k, int d, const int64_t* qs, const int64_t* ks,
+                        const int64_t* vs, const int64_t* os, int causal, float scale) {
+  mha::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.q_sb = qs[0], a.q_sh = qs[1], a.q_sn = qs[2];
+  a.k_sb = ks[0], a.k_sh = ks[1], a.k_sn = ks[2];
+  a.v_sb = vs[0], a.v_sh = vs[1], a.v_sn = vs[2];
+  a.o_sb = os[0], a.o_sh = os[1], a.o_sn = os[2];
+  a.batch = batch, a.heads = heads, a.n_q = n_q, a.n_k = n_k, a.d = d;
+  a.causal = causal;
+  a.scale = scale;
+  return a;
+}
+
+mha_status run_attention(const mha::AttnArgs& a, mha_dtype dtype, hipStream_t stream) {
+  hipError_t e = dtype == MHA_BF16 ? mha::launch_attention_bf16(a, stream) : mha::launch_attention_f32(a, stream);
+  return hip_status(e, "attention launch");
+}
+
+mha_status validate_linear(const void* x, const void* w, void* y, int m, int n, int k, int64_t ldx,
+                           int64_t ldw, int64_t ldy, int dtype) {
+  if (!x || !w || !y) return fail(MHA_ERR_INVALID_ARG, "x, w and y must be non-null");
+  if (m < 1 || n < 1 || k < 1) return fail(MHA_ERR_INVALID_ARG, "sizes must be >= 1 (m=%d n=%d k=%d)", m, n, k);
+  if (!valid_dtype(dtype)) return fail(MHA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (ldx < k || ldw < n || ldy < n)
+    return fail(MHA_ERR_INVALID_ARG, "leading dimensions too small (ldx=%lld ldw=%lld ldy=%lld)", (long long)ldx,
+                (long long)ldw, (long long)ldy);
+  const int vec = vec_elems((mha_dtype)dtype);
+  if (k % vec || n % vec || ldx % vec || ldw % vec || ldy % vec)
+    return fail(MHA_ERR_INVALID_ARG, "k, n and leading dimensions must be multiples of %d", vec);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y))
+    return fail(MHA_ERR_INVALID_ARG, "x, w and y must be 16-byte aligned");
+  const int64_t tiles = (int64_t)((m + 63) / 64) * ((n + 63) / 64);
+  if (tiles > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+  return MHA_OK;
+}
+
+mha_status run_linear(const mha::LinearArgs& a, mha_dtype dtype, hipStream_t stream) {
+  hipError_t e = dtype == MHA_BF16 ? mha::launch_linear_bf16(a, stream) : mha::launch_linear_f32(a, stream);
+  return hip_status(e, "projection launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mha_status_string(mha_status s) {
+  switch (s) {
+    case MHA_OK: return "MHA_OK";
+    case MHA_ERR_INVALID_ARG: return "MHA_ERR_INVALID_ARG";
+    case MHA_ERR_UNSUPPORTED: return "MHA_ERR_UNSUPPORTED";
+    case MHA_ERR_WORKSPACE: return "MHA_ERR_WORKSPACE";
+    case MHA_ERR_HIP: return "MHA_ERR_HIP";
+  }
+  return "MHA_ERR_UNKNOWN";
+}
+
+const char* mha_last_error(void) { return g_last_error.c_str(); }
+
+int mha_version(void) { return 100; }
+
+mha_status attention_forward(const void* q, const void* k, const void* v, void* o, int batch, int heads,
+                             int n_q, int n_k, int d_k, int d_v, const int64_t q_strides[3],
+                             const int64_t k_strides[3], const int64_t v_strides[3],
+                             const int64_t o_strides[3], mha_dtype dtype, int causal, float scale, float* lse,
+                             void* stream) {
+  try {
+    mha_status s = validate_attention(q, k, v, o, batch, heads, n_q, n_k, d_k, d_v, q_strides, k_strides,
+                                      v_strides, o_strides, (int)dtype, causal, scale);
+    if (s != MHA_OK) return s;
+    if (lse && !aligned16(lse)) return fail(MHA_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+    const mha::AttnArgs a = attn_args(q, k, v, o, lse, batch, heads, n_q, n_k, d_k, q_strides, k_strides,
+                                      v_strides, o_strides, causal, scale);
+    return run_attention(a, dtype, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in attention_forward");
+  }
+}
+
+mha_status linear_forward(const void* x, const void* w, void* y, int m, int n, int k, int64_t ldx, int64_t ldw,
+                          int64_t ldy, mha_dtype dtype, void* stream) {
+  try {
+    mha_status s = validate_linear(x, w, y, m, n, k, ldx, ldw, ldy, (int)dtype);
+    if (s != MHA_OK) return s;
+    mha::LinearArgs a = {};
+    a.g[0] = mha::LinearGroup{x, w, y, m, ldx, ldw, ldy};
+    a.groups = 1;
+    a.n = n;
+    a.k = k;
+    return run_linear(a, dtype, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in linear_forward");
+  }
+}
+
+size_t mha_forward_workspace_size(int batch, int n_q, int n_k, int d_model, int heads, mha_dtype dtype) {
+  if (batch < 1 || n_q < 1 || n_k < 1 || d_model < 1 || heads < 1 || !valid_dtype((int)dtype)) return 0;
+  WsLayout w;
+  if (!ws_layout(batch, n_q, n_k, d_model, dtype, &w)) return 0;
+  return w.total;
+}
+
+mha_status mha_forward(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk,
+                       const void* wv, const void* wo, void* out, void* workspace, size_t workspace_bytes,
+                       int batch, int n_q, int n_k, int d_model, int heads, mha_dtype dtype, int causal,
+                       void* stream) {
+  try {
+    if (!xq || !xk || !xv || !wq || !wk || !wv || !wo || !out)
+      return fail(MHA_ERR_INVALID_ARG, "inputs, weights and out must be non-null");
+    if (!workspace) return fail(MHA_ERR_INVALID_ARG, "workspace must be non-null");
+    if (batch < 1 || n_q < 1 || n_k < 1 || d_model < 1 || heads < 1)
+      return fail(MHA_ERR_INVALID_ARG, "sizes must be >= 1 (batch=%d n_q=%d n_k=%d d_model=%d heads=%d)", batch,
+                  n_q, n_k, d_model, heads);
+    if (!valid_dtype((int)dtype)) return fail(MHA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (d_model % heads)
+      return fail(MHA_ERR_INVALID_ARG, "d_model (%d) must be divisible by heads (%d)", d_model, heads);
+    if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+    if (causal && n_q != n_k)
+      return fail(MHA_ERR_INVALID_ARG, "the causal mask is defined for n_q == n_k (got %d and %d)", n_q, n_k);
+    const int d = d_model / heads;
+    mha_status s = check_head_width(dtype, d, d);
+    if (s != MHA_OK) return s;
+    const void* ptrs[9] = {xq, xk, xv, wq, wk, wv, wo, out, workspace};
+    for (const void* p : ptrs)
+      if (!aligned16(p)) return fail(MHA_ERR_INVALID_ARG, "every pointer must be 16-byte aligned");
+    WsLayout w;
+    if (!ws_layout(batch, n_q, n_k, d_model, dtype, &w))
+      return fail(MHA_ERR_UNSUPPORTED, "workspace size overflows");
+    if (workspace_bytes < w.total)
+      return fail(MHA_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.total);
+    const int64_t rows_q = (int64_t)batch * n_q, rows_k = (int64_t)batch * n_k;
+    if (rows_q > INT32_MAX || rows_k > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "batch * sequence too large");
+    if ((int64_t)batch * heads * ((n_q + 63) / 64) > INT32_MAX)
+      return fail(MHA_ERR_UNSUPPORTED, "too many (batch, head, query block) triples");
+
+    char* ws = static_cast<char*>(workspace);
+    void* qw = ws + w.q;
+    void* kw = ws + w.k;
+    void* vw = ws + w.v;
+    void* ow = ws + w.o;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    // (1) Q, K, V projections in one grouped launch; row-major (rows, d_model)
+    //     is already the head-split (batch, n, heads, d) layout.
+    mha::LinearArgs lin = {};
+    lin.g[0] = mha::LinearGroup{xq, wq, qw, (int)rows_q, d_model, d_model, d_model};
+    lin.g[1] = mha::LinearGroup{xk, wk, kw, (int)rows_k, d_model, d_model, d_model};
+    lin.g[2] = mha::LinearGroup{xv, wv, vw, (int)rows_k, d_model, d_model, d_model};
+    lin.groups = 3;
+    lin.n = d_model;
+    lin.k = d_model;
+    s = run_linear(lin, dtype, st);
+    if (s != MHA_OK) return s;
+
+    // (2) attention over the strided head views; the output lands directly in
+    //     the concatenated (batch, n_q, heads * d) layout.
+    const int64_t qs[3] = {(int64_t)n_q * d_model, d, d_model};
+    const int64_t kvs[3] = {(int64_t)n_k * d_model, d, d_model};
+    const mha::AttnArgs a = attn_args(qw, kw, vw, ow, nullptr, batch, heads, n_q, n_k, d, qs, kvs, kvs, qs,
+                                      causal, 1.0f / sqrtf((float)d));
+    s = run_attention(a, dtype, st);
+    if (s != MHA_OK) return s;
+
+    // (3) output projection W^O
+    mha::LinearArgs out_lin = {};
+    out_lin.g[0] = mha::LinearGroup{ow, wo, out, (int)rows_q, d_model, d_model, d_model};
+    out_lin.groups = 1;
+    out_lin.n = d_model;
+    out_lin.k = d_model;
+    return run_linear(out_lin, dtype, st);
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in mha_forward");
+  }
+}
+
+}  // extern "C"
