@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--workload", default="encoder", help="encoder | tiny | decoder | cross | long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the long causal attention line")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -241,6 +243,14 @@ def main():
         secondary = {"workload": wl.name, "kernel": "attn_fwd_bf16_d64", "us": round(lms * 1e3, 1),
                      "tflops": round(lt, 1), "frac_of_peak": round(lt / PEAK_BF16_TFLOPS, 4)}
         log(f"long causal attention: {lms * 1e3:.1f} us, {lt:.1f} TFLOP/s")
+
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x 256 MiB")
 
     cpu = None
     if not args.no_cpu_baseline:
