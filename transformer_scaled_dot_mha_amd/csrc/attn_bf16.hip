@@ -48,12 +48,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kD = 64;         // head width handled by this kernel
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kPitch = 72;     // LDS row pitch, bf16 elements (144 bytes: conflict-free 16-byte reads)
 constexpr int kTile = kBN * kPitch;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family: 32-bit data format)
 
 __device__ __forceinline__ u32x4 ld16(const bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -78,8 +78,205 @@ __device__ __forceinline__ int key_to_lds_row(int kappa) {
   return 8 * (2 * (kappa >> 4) + ((kappa >> 2) & 1)) + 4 * ((kappa >> 3) & 1) + (kappa & 3);
 }
 
+// max(x[lane], x[lane ^ 32]) across the two half-waves (v_permlane32_swap).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// The reference maximum moves only when a row's weights against it would
+// exceed 2^8, so the rescale of O and l is skipped on almost every tile. The
+// result is exact: numerator and denominator always use the same reference.
+constexpr float kMaxSlabSum = 256.0f;  // 2^8
+
+// Running state of one wavefront: 32 query rows, O^T in two 32-row d blocks.
+struct RowState {
+  f32x16 o0, o1;
+  float m;   // reference maximum (raw score units), identical in both lane halves
+  float mc;  // m * c
+  float l;   // running sum over this lane half's keys
+};
+
+// One 64-key tile for one wavefront, as two 32-key slabs. Both slabs' S^T
+// MFMAs are issued first; slab 0's softmax (VALU) then runs while slab 1's
+// MFMAs are in flight, and slab 1's softmax runs while slab 0's P V MFMAs are.
+// Each slab checks on its own whether the reference maximum must move; a move
+// rescales O and l after the earlier P V products have been added, so every
+// term always matches the reference it was computed against.
+// kMasked: keys past `last` (relative to this lane's first key of the tile)
+// are masked (the diagonal and the ragged end only).
+// Softmax weights of pairs [i0, i1) of one 32-key slab (16 scores per lane)
+// against the current reference, rounded to bf16; ps adds exactly the
+// rounded values.
+template <bool kMasked>
+__device__ __forceinline__ void slab_weights(const float (&sv)[16], unsigned (&pw)[8], float& ps, float mc, float c,
+                                             int i0, int i1) {
+#pragma unroll
+  for (int i = i0; i < i1; ++i) {
+    float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c, -mc));
+    float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c, -mc));
+    if (kMasked) {
+      p0 = sv[2 * i] == -INFINITY ? 0.f : p0;
+      p1 = sv[2 * i + 1] == -INFINITY ? 0.f : p1;
+    }
+    pw[i] = pack_bf16(p0, p1);
+    ps = add_pair(pw[i], ps);
+  }
+}
+
+// Every weight is <= 2^8 while the reference holds. A weight above 2^8 (or
+// an overflow) makes the lane's 16-weight sum exceed 2^8, so one compare per
+// slab detects when the reference must move; only then is the row maximum
+// formed, O and l rescaled and the slab's weights recomputed. This branch is
+// taken on the first tile and rarely after.
+template <bool kMasked>
+__device__ __forceinline__ void check_reference(RowState& st, const float (&sv)[16], unsigned (&pw)[8], float& ps,
+                                                float c) {
+  const bool bad = !(ps <= kMaxSlabSum) || st.m == -INFINITY;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
+    asm volatile("" ::: "memory");  // keep a real branch, not predicated code
+    float tmax = sv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = __builtin_fmaxf(tmax, sv[r]);
+    tmax = max_halves(tmax);
+    const float m_new = __builtin_fmaxf(st.m, tmax);
+    if (m_new > st.m) {
+      const float mc_new = m_new * c;
+      const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.mc - mc_new);
+      st.o0 *= alpha;
+      st.o1 *= alpha;
+      st.l *= alpha;
+      st.m = m_new;
+      st.mc = mc_new;
+    }
+    ps = 0.f;
+    slab_weights<kMasked>(sv, pw, ps, st.mc, c, 0, 8);
+  }
+  st.l += ps;
+}
+
+__device__ __forceinline__ void pv_step(RowState& st, const u32x4 (&vf)[2], const unsigned (&pw)[8], int jj) {
+  const bf16x8 bp = as_bf16x8(u32x4{pw[4 * jj], pw[4 * jj + 1], pw[4 * jj + 2], pw[4 * jj + 3]});
+  st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[0]), bp, st.o0, 0, 0, 0);
+  st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[1]), bp, st.o1, 0, 0, 0);
+}
+
+// One 64-key tile for one wavefront, as two 32-key slabs (register r of slab
+// holds key 32*slab + 16*(r/8) + 8*hf + r%8 of the tile).
+//
+// Unmasked tiles are issued in a fixed order so that the wavefront keeps both
+// the matrix core and the VALU busy: every MFMA is followed by a chunk of
+// softmax work that does not depend on it -
+//   slab 0's S^T MFMAs; then slab 1's four S^T MFMAs each followed by a
+//   quarter of slab 0's softmax; then slab 0's four P V MFMAs each followed by
+//   a quarter of slab 1's softmax; then slab 1's P V MFMAs.
+// A reference move (rare) rescales O and l after the earlier P V products,
+// so every term always matches the reference it was computed against.
+// kMasked (diagonal and ragged-end tiles): keys past `last`, relative to this
+// lane's first key of the tile, are masked; issued in plain program order.
+template <bool kMasked>
+__device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[4], const bf16* Ks, const bf16* Vt,
+                                            int last, int lq, int hf, float c) {
+  u32x4 kf[2][4], vf0[2][2];
+#pragma unroll
+  for (int slab = 0; slab < 2; ++slab)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf[slab][kk] = ld16(Ks + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf);
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    vf0[jj][0] = ld16(Vt + lq * kPitch + 16 * jj + 8 * hf);
+    vf0[jj][1] = ld16(Vt + (32 + lq) * kPitch + 16 * jj + 8 * hf);
+  }
+  f32x16 s0 = {}, s1 = {};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[0][kk]), as_bf16x8(qf[kk]), s0, 0, 0, 0);
+
+  float sv0[16], sv1[16];
+  unsigned pw0[8], pw1[8];
+  float ps0 = 0.f, ps1 = 0.f;
+  if (!kMasked) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[1][kk]), as_bf16x8(qf[kk]), s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv0[r] = s0[r];
+      }
+      slab_weights<false>(sv0, pw0, ps0, st.mc, c, 2 * kk, 2 * kk + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[1][kk]), as_bf16x8(qf[kk]), s1, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv0[r] = 16 * (r >> 3) + (r & 7) <= last ? s0[r] : -INFINITY;
+    slab_weights<true>(sv0, pw0, ps0, st.mc, c, 0, 8);
+  }
+  check_reference<kMasked>(st, sv0, pw0, ps0, c);
+
+  u32x4 vf1[2][2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    vf1[jj][0] = ld16(Vt + lq * kPitch + 16 * (2 + jj) + 8 * hf);
+    vf1[jj][1] = ld16(Vt + (32 + lq) * kPitch + 16 * (2 + jj) + 8 * hf);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sv1[r] = s1[r];
+    if (kMasked) sv1[r] = 32 + 16 * (r >> 3) + (r & 7) <= last ? sv1[r] : -INFINITY;
+  }
+  if (!kMasked) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const bf16x8 bp = as_bf16x8(u32x4{pw0[4 * jj], pw0[4 * jj + 1], pw0[4 * jj + 2], pw0[4 * jj + 3]});
+      st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf0[jj][0]), bp, st.o0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      slab_weights<false>(sv1, pw1, ps1, st.mc, c, 4 * jj, 4 * jj + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf0[jj][1]), bp, st.o1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      slab_weights<false>(sv1, pw1, ps1, st.mc, c, 4 * jj + 2, 4 * jj + 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    pv_step(st, vf0[0], pw0, 0);
+    pv_step(st, vf0[1], pw0, 1);
+    slab_weights<true>(sv1, pw1, ps1, st.mc, c, 0, 8);
+  }
+  check_reference<kMasked>(st, sv1, pw1, ps1, c);
+  pv_step(st, vf1[0], pw1, 0);
+  pv_step(st, vf1[1], pw1, 1);
+}
+
+// Pack lane's 4 values of d group g (d = 8g + 4hf + 0..3) of both lane halves
+// into one 16-byte row chunk: half 0 ends with group gA = 2t, half 1 with 2t+1.
+__device__ __forceinline__ u32x4 gather_row_chunk(unsigned a0, unsigned a1, unsigned b0, unsigned b1) {
+  const auto x0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+  const auto x1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+  return u32x4{(unsigned)x0[0], (unsigned)x1[0], (unsigned)x0[1], (unsigned)x1[1]};
+}
+
+#ifndef MHA_ATTN_WAVES_PER_EU
+#define MHA_ATTN_WAVES_PER_EU 2
+#endif
+
+#ifdef MHA_ATTN_OCC
+#define MHA_ATTN_OCC_ATTR __attribute__((amdgpu_waves_per_eu(MHA_ATTN_OCC, MHA_ATTN_OCC)))
+#else
+#define MHA_ATTN_OCC_ATTR
+#endif
+
 template <bool kCausal>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c, unsigned q_sign,
+__global__ __launch_bounds__(256, MHA_ATTN_WAVES_PER_EU) MHA_ATTN_OCC_ATTR void attn_fwd_bf16_d64(AttnArgs a, float c, unsigned q_sign,
                                                             int n_qblk) {
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];
 
@@ -137,17 +334,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
   // V: keys 2*(tid%32) and 2*(tid%32)+1, d chunk tid/32
   const int v_key = (tid & 31) * 2, v_chunk = tid >> 5;
 
+  // Buffer-resource loads: each thread's byte offset within a tile is fixed;
+  // the tile's base moves in scalar registers, and the descriptor's record
+  // count ends at the last valid key row, so rows past n_k read as zero with
+  // no per-lane bounds checks.
+  const int k_off[2] = {(int)(((int64_t)k_row * a.k_sn + 8 * k_chunk) * 2),
+                        (int)(((int64_t)(k_row + 32) * a.k_sn + 8 * k_chunk) * 2)};
+  const int v_off[2] = {(int)(((int64_t)v_key * a.v_sn + 8 * v_chunk) * 2),
+                        (int)(((int64_t)(v_key + 1) * a.v_sn + 8 * v_chunk) * 2)};
   u32x4 kreg[2], vreg[2];
   auto gload = [&](int k0) {
+    const int valid = min(n_k - k0, kBN);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kp + (int64_t)k0 * a.k_sn), (short)0, (int)((valid - 1) * a.k_sn * 2 + 2 * 64), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vp + (int64_t)k0 * a.v_sn), (short)0, (int)((valid - 1) * a.v_sn * 2 + 2 * 64), kBufferFlags);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int key = k0 + k_row + 32 * i;
-      kreg[i] = key < n_k ? ld16(kp + (int64_t)key * a.k_sn + 8 * k_chunk) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int key = k0 + v_key + i;
-      vreg[i] = key < n_k ? ld16(vp + (int64_t)key * a.v_sn + 8 * v_chunk) : u32x4{0, 0, 0, 0};
+      kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off[i], 0, 0));
+      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off[i], 0, 0));
     }
   };
   auto lstore = [&](int buf) {
@@ -156,114 +361,76 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       *reinterpret_cast<u32x4*>(Ks + (32 * i + k_lds) * kPitch + 8 * k_chunk) = kreg[i];
-    // V^T[d][key]: word (d, key pair) = V[key][d] | V[key+1][d] << 16
+    // V^T[d][key]: word (d, key pair) = V[key][d] | V[key+1][d] << 16 (byte permutes)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const unsigned w0 = vreg[0][e >> 1], w1 = vreg[1][e >> 1];
-      const unsigned word = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
+      const unsigned word = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
       *reinterpret_cast<unsigned*>(Vt + (8 * v_chunk + e) * kPitch + v_key) = word;
     }
   };
 
-  f32x16 o0 = {}, o1 = {};   // O^T, d rows 0..31 and 32..63, column = query lq
-  float m_run = -INFINITY;   // running max of raw scores (same in both lane halves)
-  float l_run = 0.f;         // running sum over this lane half's keys
+  RowState st;
+  st.o0 = f32x16{};
+  st.o1 = f32x16{};
+  st.m = -INFINITY;
+  st.mc = 0.f;
+  st.l = 0.f;
 
   gload(0);
   lstore(0);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Tiles before t_split are fully visible to every wavefront of the
+  // workgroup (below wavefront 0's first query and before the ragged end):
+  // they take the unmasked path. The remaining tiles (the diagonal, the end)
+  // take the masked path, or are skipped by wavefronts they lie wholly above.
+  const int t_split = min(kCausal ? qblk * (kBM / kBN) : ntiles, n_k / kBN);
+  int t = 0;
+  for (; t < t_split; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) gload((t + 1) * kBN);
+    const bf16* Ks = smem + (t & 1) * 2 * kTile;
+    attend_tile<false>(st, qf, Ks, Ks + kTile, 0, lq, hf, c);
+    if (more) lstore((t + 1) & 1);
+    __syncthreads();
+  }
+  for (; t < ntiles; ++t) {
     const int k0 = t * kBN;
     const bool more = t + 1 < ntiles;
     if (more) gload(k0 + kBN);
     const bf16* Ks = smem + (t & 1) * 2 * kTile;
-    const bf16* Vt = Ks + kTile;
-
-    if (!kCausal || k0 <= q_wave0 + 31) {
-      // ---- S^T = K Q^T for two 32-key slabs
-      f32x16 s0 = {}, s1 = {};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 bq = as_bf16x8(qf[kk]);
-        const bf16x8 a0 = as_bf16x8(ld16(Ks + lq * kPitch + 16 * kk + 8 * hf));
-        const bf16x8 a1 = as_bf16x8(ld16(Ks + (32 + lq) * kPitch + 16 * kk + 8 * hf));
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq, s1, 0, 0, 0);
-      }
-      float sv[32];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sv[r] = s0[r];
-        sv[16 + r] = s1[r];
-      }
-      // key of sv[i]: k0 + 16*(i/8) + 8*hf + i%8
-      const bool need_mask = (k0 + kBN > n_k) || (kCausal && k0 + kBN - 1 > q_wave0);
-      unsigned visible = 0xffffffffu;
-      if (need_mask) {
-        visible = 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int key = k0 + 16 * (i >> 3) + 8 * hf + (i & 7);
-          const bool ok = key < n_k && (!kCausal || key <= my_q);
-          visible |= (ok ? 1u : 0u) << i;
-          sv[i] = ok ? sv[i] : -INFINITY;
-        }
-      }
-      float tmax = sv[0];
-#pragma unroll
-      for (int i = 1; i < 32; ++i) tmax = __builtin_fmaxf(tmax, sv[i]);
-      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = __builtin_fmaxf(m_run, tmax);
-      const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(m_run, c, -mc));
-      m_run = m_new;
-
-      // ---- weights, rounded to bf16; the row sum uses the rounded values
-      unsigned pw[16];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c, -mc));
-        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c, -mc));
-        if (need_mask) {
-          p0 = (visible >> (2 * i)) & 1u ? p0 : 0.f;
-          p1 = (visible >> (2 * i + 1)) & 1u ? p1 : 0.f;
-        }
-        pw[i] = pack_bf16(p0, p1);
-        psum = add_pair(pw[i], psum);
-      }
-      l_run = __builtin_fmaf(l_run, alpha, psum);
-      o0 *= alpha;
-      o1 *= alpha;
-
-      // ---- O^T += V^T P^T, four 16-key steps
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 bp = as_bf16x8(u32x4{pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]});
-        const bf16x8 v0 = as_bf16x8(ld16(Vt + lq * kPitch + 16 * j + 8 * hf));
-        const bf16x8 v1 = as_bf16x8(ld16(Vt + (32 + lq) * kPitch + 16 * j + 8 * hf));
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, bp, o0, 0, 0, 0);
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, bp, o1, 0, 0, 0);
-      }
-    }
+    if (!kCausal || k0 <= q_wave0 + 31)  // wave-uniform
+      attend_tile<true>(st, qf, Ks, Ks + kTile, (kCausal ? min(n_k - 1, my_q) : n_k - 1) - k0 - 8 * hf, lq, hf, c);
     if (more) lstore((t + 1) & 1);
     __syncthreads();
   }
 
-  // ---- normalise and store: lane holds d = 32*blk + 8*g + 4*hf + 0..3 of query my_q
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (my_q < n_q) {
-    const float inv = 1.0f / l_tot;
-    bf16* dst = op + (int64_t)my_q * a.o_sn + 4 * hf;
+  // ---- normalise and store: lane holds d = 32*blk + 8*g + 4*hf + 0..3 of query my_q;
+  // the two halves swap groups so that each lane writes two 16-byte chunks per d block.
+  const float l_tot = sum_halves(st.l);
+  const float inv = 1.0f / l_tot;
+  unsigned w[2][4][2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      *reinterpret_cast<u32x2*>(dst + 8 * g) =
-          u32x2{pack_bf16(o0[4 * g] * inv, o0[4 * g + 1] * inv), pack_bf16(o0[4 * g + 2] * inv, o0[4 * g + 3] * inv)};
-      *reinterpret_cast<u32x2*>(dst + 32 + 8 * g) =
-          u32x2{pack_bf16(o1[4 * g] * inv, o1[4 * g + 1] * inv), pack_bf16(o1[4 * g + 2] * inv, o1[4 * g + 3] * inv)};
-    }
-    if (a.lse != nullptr && hf == 0) a.lse[(int64_t)bh * n_q + my_q] = (m_run * c + __log2f(l_tot)) * kLn2;
+  for (int g = 0; g < 4; ++g) {
+    w[0][g][0] = pack_bf16(st.o0[4 * g] * inv, st.o0[4 * g + 1] * inv);
+    w[0][g][1] = pack_bf16(st.o0[4 * g + 2] * inv, st.o0[4 * g + 3] * inv);
+    w[1][g][0] = pack_bf16(st.o1[4 * g] * inv, st.o1[4 * g + 1] * inv);
+    w[1][g][1] = pack_bf16(st.o1[4 * g + 2] * inv, st.o1[4 * g + 3] * inv);
+  }
+  u32x4 chunk[2][2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      chunk[blk][t] = gather_row_chunk(w[blk][2 * t][0], w[blk][2 * t][1], w[blk][2 * t + 1][0], w[blk][2 * t + 1][1]);
+  if (my_q < n_q) {
+    bf16* dst = op + (int64_t)my_q * a.o_sn;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<u32x4*>(dst + 32 * blk + 8 * (2 * t + hf)) = chunk[blk][t];
+    if (a.lse != nullptr && hf == 0) a.lse[(int64_t)bh * n_q + my_q] = (st.mc + __log2f(l_tot)) * kLn2;
   }
 }
 
