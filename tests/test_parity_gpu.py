@@ -112,6 +112,11 @@ EDGE = [
     (2, 2, 200, 77, False, "bf16"),
     (1, 2, 5, 300, False, "bf16"),
     (1, 1, 257, 1, False, "bf16"),
+    (2, 1, 1500, 1650, False, "bf16"),
+    # 64 query rows per wavefront (two 32-row blocks, long query runs): ragged tails
+    (1, 2, 3000, 3000, True, "bf16"),
+    (1, 1, 2500, 2600, False, "bf16"),
+    (1, 1, 4100, 4100, True, "bf16"),
     (1, 1, 1, 1, True, "f32"),
     (2, 3, 65, 65, True, "f32"),
     (1, 2, 100, 37, False, "f32"),

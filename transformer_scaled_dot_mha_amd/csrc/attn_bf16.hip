@@ -48,7 +48,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kPitch = 72;     // LDS row pitch, bf16 elements (144 bytes: conflict-free 16-byte reads)
 constexpr int kTile = kBN * kPitch;
@@ -161,100 +160,170 @@ __device__ __forceinline__ void check_reference(RowState& st, const float (&sv)[
   st.l += ps;
 }
 
-__device__ __forceinline__ void pv_step(RowState& st, const u32x4 (&vf)[2], const unsigned (&pw)[8], int jj) {
+// One P V MFMA: 16 keys (step jj of a slab) into d block blk of O^T.
+__device__ __forceinline__ void pv_one(RowState& st, const u32x4& vfrag, const unsigned (&pw)[8], int jj, int blk) {
   const bf16x8 bp = as_bf16x8(u32x4{pw[4 * jj], pw[4 * jj + 1], pw[4 * jj + 2], pw[4 * jj + 3]});
-  st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[0]), bp, st.o0, 0, 0, 0);
-  st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[1]), bp, st.o1, 0, 0, 0);
+  if (blk == 0)
+    st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfrag), bp, st.o0, 0, 0, 0);
+  else
+    st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfrag), bp, st.o1, 0, 0, 0);
 }
 
-// One 64-key tile for one wavefront, as two 32-key slabs (register r of slab
-// holds key 32*slab + 16*(r/8) + 8*hf + r%8 of the tile).
+__device__ __forceinline__ f32x16 qk_one(f32x16 acc, const u32x4& kfrag, const u32x4& qfrag) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kfrag), as_bf16x8(qfrag), acc, 0, 0, 0);
+}
+
+// Masked scores of one slab: keys past `last` (relative to this lane's first
+// key of the tile) become -inf.
+__device__ __forceinline__ void mask_slab(float (&sv)[16], const f32x16& s, int slab, int last) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sv[r] = 32 * slab + 16 * (r >> 3) + (r & 7) <= last ? s[r] : -INFINITY;
+}
+
+// One 64-key tile for one wavefront holding kQB blocks of 32 query rows.
+// Each block's tile is two 32-key slabs (register r of a slab holds key
+// 32*slab + 16*(r/8) + 8*hf + r%8 of the tile). K and V fragments are read
+// from LDS once and used by every block of the wavefront.
 //
 // Unmasked tiles are issued in a fixed order so that the wavefront keeps both
 // the matrix core and the VALU busy: every MFMA is followed by a chunk of
-// softmax work that does not depend on it -
-//   slab 0's S^T MFMAs; then slab 1's four S^T MFMAs each followed by a
-//   quarter of slab 0's softmax; then slab 0's four P V MFMAs each followed by
-//   a quarter of slab 1's softmax; then slab 1's P V MFMAs.
-// A reference move (rare) rescales O and l after the earlier P V products,
-// so every term always matches the reference it was computed against.
-// kMasked (diagonal and ragged-end tiles): keys past `last`, relative to this
-// lane's first key of the tile, are masked; issued in plain program order.
-template <bool kMasked>
-__device__ __forceinline__ void attend_tile(RowState& st, const u32x4 (&qf)[4], const bf16* Ks, const bf16* Vt,
-                                            int last, int lq, int hf, float c) {
-  u32x4 kf[2][4], vf0[2][2];
+// softmax work that does not depend on it.
+//   kQB = 1: slab 0's S^T MFMAs; slab 1's S^T MFMAs each followed by a
+//            quarter of slab 0's softmax; slab 0's P V MFMAs each followed by
+//            a quarter of slab 1's softmax; slab 1's P V MFMAs.
+//   kQB = 2: block A's S^T MFMAs; block B's eight S^T MFMAs each followed by
+//            an eighth of A's softmax; A's eight P V MFMAs each followed by an
+//            eighth of B's softmax; B's P V MFMAs.
+// A reference move (rare) rescales that block's O and l after its earlier
+// P V products, so every term matches the reference it was computed against.
+// kMasked (diagonal and ragged-end tiles) runs in plain program order.
+template <bool kMasked, int kQB>
+__device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&qf)[kQB][4], const bf16* Ks,
+                                            const bf16* Vt, const int (&last)[kQB], int lq, int hf, float c) {
+  u32x4 kf[2][4];
 #pragma unroll
   for (int slab = 0; slab < 2; ++slab)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) kf[slab][kk] = ld16(Ks + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf);
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    vf0[jj][0] = ld16(Vt + lq * kPitch + 16 * jj + 8 * hf);
-    vf0[jj][1] = ld16(Vt + (32 + lq) * kPitch + 16 * jj + 8 * hf);
-  }
-  f32x16 s0 = {}, s1 = {};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[0][kk]), as_bf16x8(qf[kk]), s0, 0, 0, 0);
 
-  float sv0[16], sv1[16];
-  unsigned pw0[8], pw1[8];
-  float ps0 = 0.f, ps1 = 0.f;
-  if (!kMasked) {
+  if (kMasked) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      f32x16 s[2] = {};
+#pragma unroll
+      for (int slab = 0; slab < 2; ++slab)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) s[slab] = qk_one(s[slab], kf[slab][kk], qf[qb][kk]);
+#pragma unroll
+      for (int slab = 0; slab < 2; ++slab) {
+        float sv[16];
+        unsigned pw[8];
+        float ps = 0.f;
+        mask_slab(sv, s[slab], slab, last[qb]);
+        slab_weights<true>(sv, pw, ps, st[qb].mc, c, 0, 8);
+        check_reference<true>(st[qb], sv, pw, ps, c);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+            pv_one(st[qb], ld16(Vt + (32 * blk + lq) * kPitch + 16 * (2 * slab + jj) + 8 * hf), pw, jj, blk);
+      }
+    }
+    return;
+  }
+
+  if (kQB == 1) {
+    u32x4 vf0[2][2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) vf0[jj][blk] = ld16(Vt + (32 * blk + lq) * kPitch + 16 * jj + 8 * hf);
+    f32x16 s0 = {}, s1 = {};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) s0 = qk_one(s0, kf[0][kk], qf[0][kk]);
+    float sv0[16], sv1[16];
+    unsigned pw0[8], pw1[8];
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[1][kk]), as_bf16x8(qf[kk]), s1, 0, 0, 0);
+      s1 = qk_one(s1, kf[1][kk], qf[0][kk]);
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sv0[r] = s0[r];
       }
-      slab_weights<false>(sv0, pw0, ps0, st.mc, c, 2 * kk, 2 * kk + 2);
+      slab_weights<false>(sv0, pw0, ps0, st[0].mc, c, 2 * kk, 2 * kk + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
-  } else {
+    check_reference<false>(st[0], sv0, pw0, ps0, c);
+    u32x4 vf1[2][2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[1][kk]), as_bf16x8(qf[kk]), s1, 0, 0, 0);
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv0[r] = 16 * (r >> 3) + (r & 7) <= last ? s0[r] : -INFINITY;
-    slab_weights<true>(sv0, pw0, ps0, st.mc, c, 0, 8);
-  }
-  check_reference<kMasked>(st, sv0, pw0, ps0, c);
-
-  u32x4 vf1[2][2];
+      for (int blk = 0; blk < 2; ++blk) vf1[jj][blk] = ld16(Vt + (32 * blk + lq) * kPitch + 16 * (2 + jj) + 8 * hf);
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    vf1[jj][0] = ld16(Vt + lq * kPitch + 16 * (2 + jj) + 8 * hf);
-    vf1[jj][1] = ld16(Vt + (32 + lq) * kPitch + 16 * (2 + jj) + 8 * hf);
-  }
+    for (int r = 0; r < 16; ++r) sv1[r] = s1[r];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    sv1[r] = s1[r];
-    if (kMasked) sv1[r] = 32 + 16 * (r >> 3) + (r & 7) <= last ? sv1[r] : -INFINITY;
-  }
-  if (!kMasked) {
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const bf16x8 bp = as_bf16x8(u32x4{pw0[4 * jj], pw0[4 * jj + 1], pw0[4 * jj + 2], pw0[4 * jj + 3]});
-      st.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf0[jj][0]), bp, st.o0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      pv_one(st[0], vf0[i >> 1][i & 1], pw0, i >> 1, i & 1);
       __builtin_amdgcn_sched_barrier(0);
-      slab_weights<false>(sv1, pw1, ps1, st.mc, c, 4 * jj, 4 * jj + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      st.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf0[jj][1]), bp, st.o1, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      slab_weights<false>(sv1, pw1, ps1, st.mc, c, 4 * jj + 2, 4 * jj + 4);
+      slab_weights<false>(sv1, pw1, ps1, st[0].mc, c, 2 * i, 2 * i + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
+    check_reference<false>(st[0], sv1, pw1, ps1, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv_one(st[0], vf1[i >> 1][i & 1], pw1, i >> 1, i & 1);
   } else {
-    pv_step(st, vf0[0], pw0, 0);
-    pv_step(st, vf0[1], pw0, 1);
-    slab_weights<true>(sv1, pw1, ps1, st.mc, c, 0, 8);
+    // block A = 0, block B = kQB - 1
+    constexpr int A = 0, B = kQB - 1;
+    f32x16 sa[2] = {}, sb[2] = {};
+#pragma unroll
+    for (int slab = 0; slab < 2; ++slab)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sa[slab] = qk_one(sa[slab], kf[slab][kk], qf[A][kk]);
+    u32x4 vf[2][2][2];  // [slab][jj][blk]
+#pragma unroll
+    for (int slab = 0; slab < 2; ++slab)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+          vf[slab][jj][blk] = ld16(Vt + (32 * blk + lq) * kPitch + 16 * (2 * slab + jj) + 8 * hf);
+    float sva[2][16], svb[2][16];
+    unsigned pwa[2][8], pwb[2][8];
+    float psa[2] = {0.f, 0.f}, psb[2] = {0.f, 0.f};
+    // B's S^T, each MFMA followed by a quarter slab of A's softmax
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slab = i >> 2, kk = i & 3;
+      sb[slab] = qk_one(sb[slab], kf[slab][kk], qf[B][kk]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sva[slab][r] = sa[slab][r];
+      }
+      slab_weights<false>(sva[slab], pwa[slab], psa[slab], st[A].mc, c, 2 * kk, 2 * kk + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 3) check_reference<false>(st[A], sva[slab], pwa[slab], psa[slab], c);
+    }
+    // A's P V, each MFMA followed by a quarter slab of B's softmax
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slab = i >> 2, jj = (i >> 1) & 1, blk = i & 1, q4 = i & 3;
+      pv_one(st[A], vf[slab][jj][blk], pwa[slab], jj, blk);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q4 == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) svb[slab][r] = sb[slab][r];
+      }
+      slab_weights<false>(svb[slab], pwb[slab], psb[slab], st[B].mc, c, 2 * q4, 2 * q4 + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q4 == 3) check_reference<false>(st[B], svb[slab], pwb[slab], psb[slab], c);
+    }
+    // B's P V
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv_one(st[B], vf[i >> 2][(i >> 1) & 1][i & 1], pwb[i >> 2], (i >> 1) & 1, i & 1);
   }
-  check_reference<kMasked>(st, sv1, pw1, ps1, c);
-  pv_step(st, vf1[0], pw1, 0);
-  pv_step(st, vf1[1], pw1, 1);
 }
 
 // Pack lane's 4 values of d group g (d = 8g + 4hf + 0..3) of both lane halves
@@ -265,19 +334,11 @@ __device__ __forceinline__ u32x4 gather_row_chunk(unsigned a0, unsigned a1, unsi
   return u32x4{(unsigned)x0[0], (unsigned)x1[0], (unsigned)x0[1], (unsigned)x1[1]};
 }
 
-#ifndef MHA_ATTN_WAVES_PER_EU
-#define MHA_ATTN_WAVES_PER_EU 2
-#endif
-
-#ifdef MHA_ATTN_OCC
-#define MHA_ATTN_OCC_ATTR __attribute__((amdgpu_waves_per_eu(MHA_ATTN_OCC, MHA_ATTN_OCC)))
-#else
-#define MHA_ATTN_OCC_ATTR
-#endif
-
-template <bool kCausal>
-__global__ __launch_bounds__(256, MHA_ATTN_WAVES_PER_EU) MHA_ATTN_OCC_ATTR void attn_fwd_bf16_d64(AttnArgs a, float c, unsigned q_sign,
-                                                            int n_qblk) {
+// kQB blocks of 32 query rows per wavefront, 4 wavefronts per workgroup.
+template <bool kCausal, int kQB>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c, unsigned q_sign, int n_qblk) {
+  constexpr int kRowsPerWave = 32 * kQB;
+  constexpr int kRows = 4 * kRowsPerWave;  // query rows per workgroup
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];
 
   const int tid = threadIdx.x;
@@ -310,21 +371,19 @@ __global__ __launch_bounds__(256, MHA_ATTN_WAVES_PER_EU) MHA_ATTN_OCC_ATTR void 
   const bf16* vp = static_cast<const bf16*>(a.v) + b * a.v_sb + h * a.v_sh;
   bf16* op = static_cast<bf16*>(a.o) + b * a.o_sb + h * a.o_sh;
 
-  const int q_wave0 = qblk * kBM + wave * 32;
-  const int my_q = q_wave0 + lq;
+  const int q_wave0 = qblk * kRows + wave * kRowsPerWave;
 
-  // ---- this lane's slice of Q^T: d = 16*kk + 8*hf + 0..7 of query my_q
-  u32x4 qf[4];
-  if (my_q < n_q) {
-    const bf16* src = qp + (int64_t)my_q * a.q_sn + 8 * hf;
+  // ---- this lane's slices of Q^T: d = 16*kk + 8*hf + 0..7 of query q_wave0 + 32*qb + lq
+  u32x4 qf[kQB][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[kk] = ld16(src + 16 * kk) ^ q_sign;
-  } else {
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int my_q = q_wave0 + 32 * qb + lq;
+    const bf16* src = qp + (int64_t)min(my_q, n_q - 1) * a.q_sn + 8 * hf;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[kk] = u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = my_q < n_q ? (ld16(src + 16 * kk) ^ q_sign) : u32x4{0, 0, 0, 0};
   }
 
-  const int kv_end = kCausal ? min(n_k, qblk * kBM + kBM) : n_k;
+  const int kv_end = kCausal ? min(n_k, qblk * kRows + kRows) : n_k;
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
   // ---- cooperative staging assignment
@@ -369,28 +428,32 @@ __global__ __launch_bounds__(256, MHA_ATTN_WAVES_PER_EU) MHA_ATTN_OCC_ATTR void 
     }
   };
 
-  RowState st;
-  st.o0 = f32x16{};
-  st.o1 = f32x16{};
-  st.m = -INFINITY;
-  st.mc = 0.f;
-  st.l = 0.f;
+  RowState st[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    st[qb].o0 = f32x16{};
+    st[qb].o1 = f32x16{};
+    st[qb].m = -INFINITY;
+    st[qb].mc = 0.f;
+    st[qb].l = 0.f;
+  }
 
   gload(0);
   lstore(0);
   __syncthreads();
 
   // Tiles before t_split are fully visible to every wavefront of the
-  // workgroup (below wavefront 0's first query and before the ragged end):
+  // workgroup (below the workgroup's first query and before the ragged end):
   // they take the unmasked path. The remaining tiles (the diagonal, the end)
   // take the masked path, or are skipped by wavefronts they lie wholly above.
-  const int t_split = min(kCausal ? qblk * (kBM / kBN) : ntiles, n_k / kBN);
+  const int t_split = min(kCausal ? qblk * (kRows / kBN) : ntiles, n_k / kBN);
+  const int no_mask[kQB] = {};
   int t = 0;
   for (; t < t_split; ++t) {
     const bool more = t + 1 < ntiles;
     if (more) gload((t + 1) * kBN);
     const bf16* Ks = smem + (t & 1) * 2 * kTile;
-    attend_tile<false>(st, qf, Ks, Ks + kTile, 0, lq, hf, c);
+    attend_tile<false, kQB>(st, qf, Ks, Ks + kTile, no_mask, lq, hf, c);
     if (more) lstore((t + 1) & 1);
     __syncthreads();
   }
@@ -399,53 +462,82 @@ __global__ __launch_bounds__(256, MHA_ATTN_WAVES_PER_EU) MHA_ATTN_OCC_ATTR void 
     const bool more = t + 1 < ntiles;
     if (more) gload(k0 + kBN);
     const bf16* Ks = smem + (t & 1) * 2 * kTile;
-    if (!kCausal || k0 <= q_wave0 + 31)  // wave-uniform
-      attend_tile<true>(st, qf, Ks, Ks + kTile, (kCausal ? min(n_k - 1, my_q) : n_k - 1) - k0 - 8 * hf, lq, hf, c);
+    if (!kCausal || k0 <= q_wave0 + kRowsPerWave - 1) {  // wave-uniform
+      int last[kQB];
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        last[qb] = (kCausal ? min(n_k - 1, q_wave0 + 32 * qb + lq) : n_k - 1) - k0 - 8 * hf;
+      attend_tile<true, kQB>(st, qf, Ks, Ks + kTile, last, lq, hf, c);
+    }
     if (more) lstore((t + 1) & 1);
     __syncthreads();
   }
 
-  // ---- normalise and store: lane holds d = 32*blk + 8*g + 4*hf + 0..3 of query my_q;
+  // ---- normalise and store: lane holds d = 32*blk + 8*g + 4*hf + 0..3 of its query;
   // the two halves swap groups so that each lane writes two 16-byte chunks per d block.
-  const float l_tot = sum_halves(st.l);
-  const float inv = 1.0f / l_tot;
-  unsigned w[2][4][2];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    w[0][g][0] = pack_bf16(st.o0[4 * g] * inv, st.o0[4 * g + 1] * inv);
-    w[0][g][1] = pack_bf16(st.o0[4 * g + 2] * inv, st.o0[4 * g + 3] * inv);
-    w[1][g][0] = pack_bf16(st.o1[4 * g] * inv, st.o1[4 * g + 1] * inv);
-    w[1][g][1] = pack_bf16(st.o1[4 * g + 2] * inv, st.o1[4 * g + 3] * inv);
-  }
-  u32x4 chunk[2][2];
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int my_q = q_wave0 + 32 * qb + lq;
+    const float l_tot = sum_halves(st[qb].l);
+    const float inv = 1.0f / l_tot;
+    unsigned w[2][4][2];
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      chunk[blk][t] = gather_row_chunk(w[blk][2 * t][0], w[blk][2 * t][1], w[blk][2 * t + 1][0], w[blk][2 * t + 1][1]);
-  if (my_q < n_q) {
-    bf16* dst = op + (int64_t)my_q * a.o_sn;
+    for (int g = 0; g < 4; ++g) {
+      w[0][g][0] = pack_bf16(st[qb].o0[4 * g] * inv, st[qb].o0[4 * g + 1] * inv);
+      w[0][g][1] = pack_bf16(st[qb].o0[4 * g + 2] * inv, st[qb].o0[4 * g + 3] * inv);
+      w[1][g][0] = pack_bf16(st[qb].o1[4 * g] * inv, st[qb].o1[4 * g + 1] * inv);
+      w[1][g][1] = pack_bf16(st[qb].o1[4 * g + 2] * inv, st[qb].o1[4 * g + 3] * inv);
+    }
+    u32x4 chunk[2][2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        *reinterpret_cast<u32x4*>(dst + 32 * blk + 8 * (2 * t + hf)) = chunk[blk][t];
-    if (a.lse != nullptr && hf == 0) a.lse[(int64_t)bh * n_q + my_q] = (st.mc + __log2f(l_tot)) * kLn2;
+      for (int tt = 0; tt < 2; ++tt)
+        chunk[blk][tt] =
+            gather_row_chunk(w[blk][2 * tt][0], w[blk][2 * tt][1], w[blk][2 * tt + 1][0], w[blk][2 * tt + 1][1]);
+    if (my_q < n_q) {
+      bf16* dst = op + (int64_t)my_q * a.o_sn;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          *reinterpret_cast<u32x4*>(dst + 32 * blk + 8 * (2 * tt + hf)) = chunk[blk][tt];
+      if (a.lse != nullptr && hf == 0) a.lse[(int64_t)bh * n_q + my_q] = (st[qb].mc + __log2f(l_tot)) * kLn2;
+    }
   }
 }
 
 }  // namespace
 
+// Rows per wavefront: 64 (two 32-row blocks share every K/V fragment read)
+// for long query runs with little padding in 256-row workgroups, else 32.
+// Measured on MI355X: 64 rows pay off from a few thousand queries on (longer
+// K/V streams per workgroup); for short runs the 32-row form's extra
+// occupancy and finer causal split win.
+int attention_rows_per_wave(int n_q) {
+  const int pad256 = (n_q + 255) / 256 * 256 - n_q;
+  return (n_q >= 2048 && pad256 * 16 <= n_q) ? 64 : 32;
+}
+
+template <int kQB>
+static void launch_qb(const AttnArgs& a, hipStream_t stream, float c, unsigned q_sign) {
+  const int rows = 4 * 32 * kQB;
+  const int n_qblk = (a.n_q + rows - 1) / rows;
+  const dim3 grid((unsigned)(n_qblk * a.batch * a.heads));
+  if (a.causal)
+    hipLaunchKernelGGL((attn_fwd_bf16_d64<true, kQB>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_d64<false, kQB>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+}
+
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
   const float kLog2e = 1.4426950408889634f;
   const float c = fabsf(a.scale) * kLog2e;
   const unsigned q_sign = a.scale < 0.f ? 0x80008000u : 0u;  // negate Q exactly: scale*s = |scale|*(-q).k
-  const int n_qblk = (a.n_q + kBM - 1) / kBM;
-  const dim3 grid((unsigned)(n_qblk * a.batch * a.heads));
-  if (a.causal)
-    hipLaunchKernelGGL(attn_fwd_bf16_d64<true>, grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+  if (attention_rows_per_wave(a.n_q) == 64)
+    launch_qb<2>(a, stream, c, q_sign);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_d64<false>, grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+    launch_qb<1>(a, stream, c, q_sign);
   return hipGetLastError();
 }
 
