@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -49,8 +50,14 @@ def log(msg):
 
 
 def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code: comments and blank lines do not count,
+    so a comment edit keeps the recorded counters valid."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def torch_tensor(stored, dev):
@@ -218,7 +225,10 @@ def main():
     value = flops_step / (ms * 1e-3) / 1e12
     log(f"step {ms * 1e3:.1f} us, {value:.1f} TFLOP/s")
 
-    dom_ms = time_events(dom_fn, max(args.steps, 20), stream)
+    # attention-only workloads: the timed step is the one attention launch, so its
+    # average duration is the step time itself; an MHA step re-times its attention
+    # launch alone on the same workspace views
+    dom_ms = ms if dom_fn is step else time_events(dom_fn, max(args.steps, 20), stream)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     launch_desc = f"{dom_name}:{w.name}"

@@ -8,10 +8,12 @@
 // "32 Transformer", "Connections"; re-derived here for CDNA4).
 //
 // Work decomposition
-//   workgroup = 256 threads = 4 wavefronts; it owns 128 query rows of one
-//   (batch, head); each wavefront owns 32 of them.
+//   workgroup = 256 threads = 4 wavefronts of one (batch, head); each
+//   wavefront owns 32 query rows, or 64 (two 32-row blocks sharing every K/V
+//   fragment read) for long query runs, so a workgroup owns 128 or 256 rows.
 //   key/value tiles of 64 rows are staged through LDS, double buffered, with
-//   the next tile's global loads in flight while the current one is used.
+//   the next tile's global loads (raw buffer loads; rows past the end read as
+//   zero) in flight while the current one is used.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, fp32 accumulate)
 //   Scores are formed transposed, S^T = K Q^T: the MFMA's B operand is the
@@ -28,7 +30,10 @@
 //
 // Softmax: exp2 with scale*log2(e) folded into one FMA; the row sum is
 // accumulated from the bf16-rounded weights that the P V product uses, so the
-// final 1/l normalises exactly what was summed.
+// final 1/l normalises exactly what was summed. The reference maximum is
+// moved lazily (only when weights against it would grow past 2^8), so the
+// rescale of O and l is skipped on almost every tile; numerator and
+// denominator always share one reference, so the result stays exact.
 // Causal: tiles wholly above the diagonal are never loaded; per wavefront, a
 // tile whose first key lies past the wavefront's last query is skipped; only
 // tiles that straddle the diagonal (or the ragged end) apply per-element masks.
@@ -94,7 +99,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 // result is exact: numerator and denominator always use the same reference.
 constexpr float kMaxSlabSum = 256.0f;  // 2^8
 
-// Running state of one wavefront: 32 query rows, O^T in two 32-row d blocks.
+// Running state of one 32-row query block: O^T in two 32-row d blocks.
 struct RowState {
   f32x16 o0, o1;
   float m;   // reference maximum (raw score units), identical in both lane halves
@@ -102,14 +107,6 @@ struct RowState {
   float l;   // running sum over this lane half's keys
 };
 
-// One 64-key tile for one wavefront, as two 32-key slabs. Both slabs' S^T
-// MFMAs are issued first; slab 0's softmax (VALU) then runs while slab 1's
-// MFMAs are in flight, and slab 1's softmax runs while slab 0's P V MFMAs are.
-// Each slab checks on its own whether the reference maximum must move; a move
-// rescales O and l after the earlier P V products have been added, so every
-// term always matches the reference it was computed against.
-// kMasked: keys past `last` (relative to this lane's first key of the tile)
-// are masked (the diagonal and the ragged end only).
 // Softmax weights of pairs [i0, i1) of one 32-key slab (16 scores per lane)
 // against the current reference, rounded to bf16; ps adds exactly the
 // rounded values.
