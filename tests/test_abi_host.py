@@ -136,6 +136,8 @@ def test_workspace_size_arithmetic(lib):
     (dict(ldx=8), _lib.MHA_ERR_INVALID_ARG),
     (dict(y=MIS), _lib.MHA_ERR_INVALID_ARG),
     (dict(dtype=3), _lib.MHA_ERR_INVALID_ARG),
+    (dict(ldx=(1 << 21) + 8), _lib.MHA_ERR_UNSUPPORTED),
+    (dict(ldw=(1 << 23) + 8), _lib.MHA_ERR_UNSUPPORTED),
 ])
 def test_linear_validation(lib, kw, status):
     a = dict(x=FAKE, w=FAKE, y=FAKE, m=64, n=64, k=64, ldx=64, ldw=64, ldy=64, dtype=_lib.MHA_BF16)

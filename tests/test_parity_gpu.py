@@ -230,7 +230,8 @@ def test_key_permutation_invariance_on_gpu(dev):
 
 # ---------------------------------------------------------------- projections and full MHA variants
 @pytest.mark.parametrize("m,n,k,dtype", [(1, 8, 8, "bf16"), (300, 136, 72, "bf16"), (2048, 512, 512, "bf16"),
-                                         (37, 20, 12, "f32"), (129, 512, 512, "f32")])
+                                         (257, 520, 136, "bf16"), (1000, 1536, 512, "bf16"), (64, 128, 1040, "bf16"),
+                                         (16384, 512, 512, "bf16"), (37, 20, 12, "f32"), (129, 512, 512, "f32")])
 def test_linear_parity(dev, m, n, k, dtype):
     import torch
     x = workloads.random_tensor((m, k), dtype, seed=31)
@@ -239,6 +240,22 @@ def test_linear_parity(dev, m, n, k, dtype):
     y = mha.linear_forward(to_device(x, dev), to_device(wt, dev))
     torch.cuda.synchronize()
     assert_close(to_f64(y), oracle.linear_ref(x.value, wt.value), dtype, "linear")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_linear_strided(dev, dtype):
+    """Leading dimensions wider than the row: X, W and Y are column slices of wider buffers."""
+    import torch
+    m, n, k = 333, 200, 264
+    xb = workloads.random_tensor((m, k + 24), dtype, seed=33)
+    wb = workloads.random_tensor((k, n + 40), dtype, seed=34, scale=1 / math.sqrt(k))
+    x, w = to_device(xb, dev)[:, :k], to_device(wb, dev)[:, :n]
+    yb = torch.full((m, n + 16), 7.0, dtype=x.dtype, device=dev)
+    say(f"linear strided {dtype}")
+    mha.linear_forward(x, w, out=yb[:, :n])
+    torch.cuda.synchronize()
+    assert_close(to_f64(yb[:, :n]), oracle.linear_ref(xb.value[:, :k], wb.value[:, :n]), dtype, "linear strided")
+    assert bool((yb[:, n:] == 7.0).all()), "write outside the output view"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -7,15 +7,24 @@
 // Because head i owns columns [i*d, (i+1)*d), the row-major Y already *is* the
 // head-split (batch, n, heads, d) layout; no permutation pass is needed.
 //
-// Tile 128 x 128 per workgroup, 32-deep k steps, double-buffered LDS.
-// 4 wavefronts in a 2 x 2 arrangement, each owning 64 x 64 outputs as 2 x 2
-// blocks of v_mfma_f32_32x32x16_bf16. The MFMA computes Y^T blocks
-// (A operand = W^T rows, B operand = X^T columns) so that each lane ends with
-// 4 consecutive output columns of one row and stores 8 contiguous bytes.
-// W's k dimension is strided in memory; it is transposed into LDS while
-// staging, two k rows packed per 32-bit word.
-// Up to three independent problems sharing n and k run in one launch
-// (grid.y selects the problem): the Q, K and V projections together.
+// Tile 256 x 128 per workgroup of 4 wavefronts; wavefront w owns rows
+// 64*w .. +63 and all 128 columns as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16,
+// so every fragment read from LDS feeds two or four MFMAs (0.75 KB of LDS
+// reads per MFMA; a 64 x 64 wavefront tile would need 1 KB, the LDS's whole
+// rate at full MFMA issue). The MFMA computes Y^T blocks: its A operand is a
+// 32 x 16 slice of W^T, its B operand a 16 x 32 slice of X^T, and each lane
+// ends with 4 consecutive columns of one row.
+// X and W are staged through LDS in 64-deep k chunks, double buffered, with
+// the next chunk's global loads in flight during the MFMAs. X rows are copied
+// as they are (coalesced 16-byte loads, 144-byte LDS rows for conflict-free
+// fragment reads); W is read row-major and transposed while it is written
+// (four k values per column, 8 bytes), so every fragment is one 16-byte read.
+// Raw buffer loads bound every read: rows past m, k past the last column and
+// rows of W past k read as zero, with no per-lane bounds branches.
+// Up to three independent problems sharing n and k run in one launch (the Q,
+// K and V projections); the workgroup order puts the column tiles and groups
+// of one row tile on one XCD, so that a self-attention X row tile is fetched
+// from HBM once.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -31,115 +40,148 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTM = 128, kTN = 128, kTK = 32;
-constexpr int kPitch = 40;  // LDS row pitch in elements (80 bytes)
+constexpr int kTM = 256, kTN = 128, kTK = 64;
+constexpr int kPitch = 72;  // LDS row pitch in elements (144 bytes: conflict-free 16-byte reads)
 constexpr int kXTile = kTM * kPitch;
 constexpr int kWTile = kTN * kPitch;
+constexpr int kStage = kXTile + kWTile;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family: 32-bit data format)
+constexpr unsigned kOutOfRange = 0x80000000u;  // byte offset past any record count: the load returns zero
 
-__device__ __forceinline__ u32x4 ld16(const bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   f32x2 f = {lo, hi};
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
 }
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// Pack a lane's 4 values of column group g (columns 8g + 4hf + 0..3) of both
+// lane halves into one 16-byte row chunk: half 0 ends with group 2t, half 1
+// with group 2t + 1.
+__device__ __forceinline__ u32x4 gather_row_chunk(unsigned a0, unsigned a1, unsigned b0, unsigned b1) {
+  const auto x0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+  const auto x1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+  return u32x4{(unsigned)x0[0], (unsigned)x1[0], (unsigned)x0[1], (unsigned)x1[1]};
+}
 
-__global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, int tiles_n, int tiles_m) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (kXTile + kWTile)];
-  // uniform selects, not a dynamic index into the kernel arguments
-  const LinearGroup g = blockIdx.y == 0 ? args.g[0] : (blockIdx.y == 1 ? args.g[1] : args.g[2]);
-  const int n = args.n, kdim = args.k;
+__global__ __launch_bounds__(256, 1) void linear_bf16_kernel(LinearArgs args, int tiles_n, int tiles_m) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * kStage];
+  const int n = args.n, kdim = args.k, groups = args.groups;
 
-  // XCD-aware order: each XCD gets a contiguous run of tiles, n fastest, so
-  // the column tiles of one row tile share an L2 (and the X tile it holds).
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; each XCD
+  // gets a contiguous run of logical ids, ordered (row tile, group, column
+  // tile) with the column tile fastest.
   const int total = gridDim.x, id = blockIdx.x;
-  const int per = total >> 3, rem = total & 7, x = id & 7, slot = id >> 3;
-  const int logical = (x < rem) ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
-  const int tm = logical / tiles_n, tn = logical - tm * tiles_n;
+  const int per = total >> 3, rem = total & 7, xcd = id & 7, slot = id >> 3;
+  const int logical = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int tn = logical % tiles_n;
+  const int rest = logical / tiles_n;
+  const int gi = rest % groups, tm = rest / groups;
+  const LinearGroup g = gi == 0 ? args.g[0] : (gi == 1 ? args.g[1] : args.g[2]);
   const int m0 = tm * kTM, n0 = tn * kTN;
-  if (tm >= tiles_m || m0 >= g.m) return;
+  if (tm >= tiles_m || m0 >= g.m) return;  // workgroup-uniform
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hf = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
-  const bf16* X = static_cast<const bf16*>(g.x);
-  const bf16* W = static_cast<const bf16*>(g.w);
+  const bf16* X = static_cast<const bf16*>(g.x) + (int64_t)m0 * g.ldx;
+  const bf16* W = static_cast<const bf16*>(g.w) + n0;
   bf16* Y = static_cast<bf16*>(g.y);
+  const int valid_m = min(kTM, g.m - m0);
+  const int valid_n = min(kTN, n - n0);
 
-  // staging assignment: X rows tid/4 and tid/4+64, 16-byte chunk tid%4;
-  // W k rows 2*(tid%16) and +1, 8-column chunk tid/16
-  const int x_row = tid >> 2, x_chunk = tid & 3;
-  const int w_k = (tid & 15) * 2, w_chunk = tid >> 4;
+  // X staging: 16-byte chunk tid%8 of rows tid/8 + 32*i
+  const int x_c = tid & 7, x_r = tid >> 3;
+  // W staging: k rows 4*(tid%16) + 0..3, 8-column chunk tid/16; written
+  // transposed as W^T[n][k .. k+3] (8 bytes per column)
+  const int w_q = tid & 15, w_c = tid >> 4;
+  const unsigned w_off = (unsigned)(((int64_t)(4 * w_q) * g.ldw + 8 * w_c) * 2);
 
-  u32x4 xr[2], wr[2];
+  u32x4 xr[8], wr[4];
   auto gload = [&](int k0) {
+    const int cols = min(kTK, kdim - k0);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(X + k0), (short)0, (int)(((int64_t)(valid_m - 1) * g.ldx + cols) * 2), kBufferFlags);
+    // k past the last column would read the next row's values: force zero
+    const unsigned xo = 8 * x_c < cols ? (unsigned)(((int64_t)x_r * g.ldx + 8 * x_c) * 2) : kOutOfRange;
+    const unsigned xstep = (unsigned)(32 * g.ldx * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = m0 + x_row + 64 * i, col = k0 + 8 * x_chunk;
-      xr[i] = (row < g.m && col < kdim) ? ld16(X + (int64_t)row * g.ldx + col) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 8; ++i) xr[i] = bload(rx, xo == kOutOfRange ? kOutOfRange : xo + i * xstep);
+    const int rows = min(kTK, kdim - k0);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W + (int64_t)k0 * g.ldw), (short)0, (int)(((int64_t)(rows - 1) * g.ldw + valid_n) * 2), kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = k0 + w_k + i, col = n0 + 8 * w_chunk;
-      wr[i] = (row < kdim && col < n) ? ld16(W + (int64_t)row * g.ldw + col) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 4; ++i) wr[i] = bload(rw, w_off + (unsigned)(i * g.ldw * 2));
   };
   auto lstore = [&](int buf) {
-    bf16* Xs = smem + buf * (kXTile + kWTile);
+    bf16* Xs = smem + buf * kStage;
     bf16* Wt = Xs + kXTile;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(Xs + (x_row + 64 * i) * kPitch + 8 * x_chunk) = xr[i];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(Xs + (x_r + 32 * i) * kPitch + 8 * x_c) = xr[i];
+    // column n = 8*w_c + e: (W[k][n], W[k+1][n]) and (W[k+2][n], W[k+3][n]) via byte permutes
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const unsigned w0 = wr[0][e >> 1], w1 = wr[1][e >> 1];
-      const unsigned word = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
-      *reinterpret_cast<unsigned*>(Wt + (8 * w_chunk + e) * kPitch + w_k) = word;
+      const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const u32x2 v = {__builtin_amdgcn_perm(wr[1][e >> 1], wr[0][e >> 1], sel),
+                       __builtin_amdgcn_perm(wr[3][e >> 1], wr[2][e >> 1], sel)};
+      *reinterpret_cast<u32x2*>(Wt + (8 * w_c + e) * kPitch + 4 * w_q) = v;
     }
   };
 
-  f32x16 acc[2][2] = {};  // [n block][m block], Y^T layout
-  const int nsteps = (kdim + kTK - 1) / kTK;
+  f32x16 acc[4][2] = {};  // [n block][m block], Y^T layout
+  auto compute = [&](int buf) {
+    const bf16* Xs = smem + buf * kStage;
+    const bf16* Wt = Xs + kXTile;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 xf[2], wf[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        xf[mb] = *reinterpret_cast<const u32x4*>(Xs + (64 * wave + 32 * mb + lq) * kPitch + 16 * s + 8 * hf);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        wf[nb] = *reinterpret_cast<const u32x4*>(Wt + (32 * nb + lq) * kPitch + 16 * s + 8 * hf);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wf[nb]), as_bf16x8(xf[mb]), acc[nb][mb],
+                                                                0, 0, 0);
+    }
+  };
+
+  const int nchunks = (kdim + kTK - 1) / kTK;
   gload(0);
   lstore(0);
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const bool more = s + 1 < nsteps;
-    if (more) gload((s + 1) * kTK);
-    const bf16* Xs = smem + (s & 1) * (kXTile + kWTile);
-    const bf16* Wt = Xs + kXTile;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 xf[2], wf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        xf[i] = as_bf16x8(ld16(Xs + (64 * wm + 32 * i + lq) * kPitch + 16 * ks + 8 * hf));
-        wf[i] = as_bf16x8(ld16(Wt + (64 * wn + 32 * i + lq) * kPitch + 16 * ks + 8 * hf));
-      }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[nb][mb], 0, 0, 0);
-    }
-    if (more) lstore((s + 1) & 1);
+  for (int c = 0; c < nchunks; ++c) {
+    const bool more = c + 1 < nchunks;
+    if (more) gload((c + 1) * kTK);
+    compute(c & 1);
+    if (more) lstore((c + 1) & 1);
     __syncthreads();
   }
 
-  // lane holds row m0 + 64*wm + 32*mb + lq, columns n0 + 64*wn + 32*nb + 8*q + 4*hf + 0..3
+  // lane holds row 64*wave + 32*mb + lq and columns 32*nb + 8*q + 4*hf + 0..3;
+  // the two halves swap groups so that each lane writes 16-byte row chunks.
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const int row = m0 + 64 * wm + 32 * mb + lq;
-    if (row >= g.m) continue;
+    const int row = 64 * wave + 32 * mb + lq;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x16& v = acc[nb][mb];
+      unsigned w[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = n0 + 64 * wn + 32 * nb + 8 * q + 4 * hf;
-        if (col < n) {
-          const f32x16& c = acc[nb][mb];
-          *reinterpret_cast<u32x2*>(Y + (int64_t)row * g.ldy + col) =
-              u32x2{pack_bf16(c[4 * q], c[4 * q + 1]), pack_bf16(c[4 * q + 2], c[4 * q + 3])};
-        }
+        w[q][0] = pack_bf16(v[4 * q], v[4 * q + 1]);
+        w[q][1] = pack_bf16(v[4 * q + 2], v[4 * q + 3]);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 chunk = gather_row_chunk(w[2 * t][0], w[2 * t][1], w[2 * t + 1][0], w[2 * t + 1][1]);
+        const int col = 32 * nb + 16 * t + 8 * hf;
+        if (row < valid_m && col < valid_n)
+          *reinterpret_cast<u32x4*>(Y + (int64_t)(m0 + row) * g.ldy + n0 + col) = chunk;
       }
     }
   }
@@ -152,7 +194,7 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream) {
   for (int i = 0; i < a.groups; ++i) max_m = a.g[i].m > max_m ? a.g[i].m : max_m;
   const int tiles_n = (a.n + kTN - 1) / kTN;
   const int tiles_m = (max_m + kTM - 1) / kTM;
-  const dim3 grid((unsigned)(tiles_n * tiles_m), (unsigned)a.groups);
+  const dim3 grid((unsigned)(tiles_n * tiles_m * a.groups));
   hipLaunchKernelGGL(linear_bf16_kernel, grid, dim3(256), 0, stream, a, tiles_n, tiles_m);
   return hipGetLastError();
 }

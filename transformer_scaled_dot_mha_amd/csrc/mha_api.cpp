@@ -42,6 +42,8 @@ bool valid_dtype(int t) { return t == MHA_F32 || t == MHA_BF16; }
 bool f32_head_width(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxLdX = (int64_t)1 << 21;  // elements
+constexpr int64_t kMaxLdW = (int64_t)1 << 23;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace regions of mha_forward: Q, K, V, concatenated heads.
@@ -146,6 +148,11 @@ mha_status validate_linear(const void* x, const void* w, void* y, int m, int n, 
     return fail(MHA_ERR_INVALID_ARG, "x, w and y must be 16-byte aligned");
   const int64_t tiles = (int64_t)((m + 63) / 64) * ((n + 63) / 64);
   if (tiles > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+  // the bf16 kernel addresses a 256-row slice of X and a 64-row slice of W
+  // with 32-bit byte offsets
+  if (ldx > kMaxLdX || ldw > kMaxLdW)
+    return fail(MHA_ERR_UNSUPPORTED, "leading dimension too large (ldx=%lld, at most %lld; ldw=%lld, at most %lld)",
+                (long long)ldx, (long long)kMaxLdX, (long long)ldw, (long long)kMaxLdW);
   return MHA_OK;
 }
 
@@ -231,6 +238,7 @@ mha_status mha_forward(const void* xq, const void* xk, const void* xv, const voi
     if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
     if (causal && n_q != n_k)
       return fail(MHA_ERR_INVALID_ARG, "the causal mask is defined for n_q == n_k (got %d and %d)", n_q, n_k);
+    if (d_model > kMaxLdX) return fail(MHA_ERR_UNSUPPORTED, "d_model (%d) too large, at most %lld", d_model, (long long)kMaxLdX);
     const int d = d_model / heads;
     mha_status s = check_head_width(dtype, d, d);
     if (s != MHA_OK) return s;
