@@ -114,6 +114,9 @@ EDGE = [
     (1, 1, 257, 1, False, "bf16"),
     (2, 1, 1500, 1650, False, "bf16"),
     # 64 query rows per wavefront (two 32-row blocks, long query runs): ragged tails
+    (2, 2, 2048, 2048, True, "bf16"),
+    (1, 1, 2049, 2049, True, "bf16"),
+    (1, 3, 2600, 2600, True, "bf16"),
     (1, 2, 3000, 3000, True, "bf16"),
     (1, 1, 2500, 2600, False, "bf16"),
     (1, 1, 4100, 4100, True, "bf16"),

@@ -14,11 +14,13 @@
 // rate at full MFMA issue). The MFMA computes Y^T blocks: its A operand is a
 // 32 x 16 slice of W^T, its B operand a 16 x 32 slice of X^T, and each lane
 // ends with 4 consecutive columns of one row.
-// X and W are staged through LDS in 64-deep k chunks, double buffered, with
-// the next chunk's global loads in flight during the MFMAs. X rows are copied
-// as they are (coalesced 16-byte loads, 144-byte LDS rows for conflict-free
-// fragment reads); W is read row-major and transposed while it is written
-// (four k values per column, 8 bytes), so every fragment is one 16-byte read.
+// X and W are staged through LDS in 32-deep k chunks, double buffered (60 KB),
+// with the next chunk's global loads in flight during the MFMAs; two
+// workgroups share a CU, so one computes while the other waits on its loads.
+// X rows are copied as they are (coalesced 16-byte loads, 80-byte LDS rows for
+// conflict-free fragment reads); W is read row-major and transposed while it
+// is written (two k values per column, 4 bytes), so every fragment is one
+// 16-byte read.
 // Raw buffer loads bound every read: rows past m, k past the last column and
 // rows of W past k read as zero, with no per-lane bounds branches.
 // Up to three independent problems sharing n and k run in one launch (the Q,
@@ -40,8 +42,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTM = 256, kTN = 128, kTK = 64;
-constexpr int kPitch = 72;  // LDS row pitch in elements (144 bytes: conflict-free 16-byte reads)
+constexpr int kTM = 256, kTN = 128, kTK = 32;
+constexpr int kPitch = 40;  // LDS row pitch in elements (144 bytes: conflict-free 16-byte reads)
 constexpr int kXTile = kTM * kPitch;
 constexpr int kWTile = kTN * kPitch;
 constexpr int kStage = kXTile + kWTile;
@@ -65,7 +67,7 @@ __device__ __forceinline__ u32x4 gather_row_chunk(unsigned a0, unsigned a1, unsi
   return u32x4{(unsigned)x0[0], (unsigned)x1[0], (unsigned)x0[1], (unsigned)x1[1]};
 }
 
-__global__ __launch_bounds__(256, 1) void linear_bf16_kernel(LinearArgs args, int tiles_n, int tiles_m) {
+__global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, int tiles_n, int tiles_m) {
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * kStage];
   const int n = args.n, kdim = args.k, groups = args.groups;
 
@@ -90,41 +92,38 @@ __global__ __launch_bounds__(256, 1) void linear_bf16_kernel(LinearArgs args, in
   const int valid_m = min(kTM, g.m - m0);
   const int valid_n = min(kTN, n - n0);
 
-  // X staging: 16-byte chunk tid%8 of rows tid/8 + 32*i
-  const int x_c = tid & 7, x_r = tid >> 3;
-  // W staging: k rows 4*(tid%16) + 0..3, 8-column chunk tid/16; written
-  // transposed as W^T[n][k .. k+3] (8 bytes per column)
+  // X staging: 16-byte chunk tid%4 of rows tid/4 + 64*i
+  const int x_c = tid & 3, x_r = tid >> 2;
+  // W staging: k rows 2*(tid%16) + 0..1, 8-column chunk tid/16
   const int w_q = tid & 15, w_c = tid >> 4;
-  const unsigned w_off = (unsigned)(((int64_t)(4 * w_q) * g.ldw + 8 * w_c) * 2);
+  const unsigned w_off = (unsigned)(((int64_t)(2 * w_q) * g.ldw + 8 * w_c) * 2);
 
-  u32x4 xr[8], wr[4];
+  u32x4 xr[4], wr[2];
   auto gload = [&](int k0) {
     const int cols = min(kTK, kdim - k0);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(X + k0), (short)0, (int)(((int64_t)(valid_m - 1) * g.ldx + cols) * 2), kBufferFlags);
     // k past the last column would read the next row's values: force zero
     const unsigned xo = 8 * x_c < cols ? (unsigned)(((int64_t)x_r * g.ldx + 8 * x_c) * 2) : kOutOfRange;
-    const unsigned xstep = (unsigned)(32 * g.ldx * 2);
+    const unsigned xstep = (unsigned)(64 * g.ldx * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xr[i] = bload(rx, xo == kOutOfRange ? kOutOfRange : xo + i * xstep);
+    for (int i = 0; i < 4; ++i) xr[i] = bload(rx, xo == kOutOfRange ? kOutOfRange : xo + i * xstep);
     const int rows = min(kTK, kdim - k0);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(W + (int64_t)k0 * g.ldw), (short)0, (int)(((int64_t)(rows - 1) * g.ldw + valid_n) * 2), kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wr[i] = bload(rw, w_off + (unsigned)(i * g.ldw * 2));
+    for (int i = 0; i < 2; ++i) wr[i] = bload(rw, w_off + (unsigned)(i * g.ldw * 2));
   };
   auto lstore = [&](int buf) {
     bf16* Xs = smem + buf * kStage;
     bf16* Wt = Xs + kXTile;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(Xs + (x_r + 32 * i) * kPitch + 8 * x_c) = xr[i];
-    // column n = 8*w_c + e: (W[k][n], W[k+1][n]) and (W[k+2][n], W[k+3][n]) via byte permutes
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(Xs + (x_r + 64 * i) * kPitch + 8 * x_c) = xr[i];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const u32x2 v = {__builtin_amdgcn_perm(wr[1][e >> 1], wr[0][e >> 1], sel),
-                       __builtin_amdgcn_perm(wr[3][e >> 1], wr[2][e >> 1], sel)};
-      *reinterpret_cast<u32x2*>(Wt + (8 * w_c + e) * kPitch + 4 * w_q) = v;
+      *reinterpret_cast<unsigned*>(Wt + (8 * w_c + e) * kPitch + 2 * w_q) =
+          __builtin_amdgcn_perm(wr[1][e >> 1], wr[0][e >> 1], sel);
     }
   };
 
@@ -133,7 +132,7 @@ __global__ __launch_bounds__(256, 1) void linear_bf16_kernel(LinearArgs args, in
     const bf16* Xs = smem + buf * kStage;
     const bf16* Wt = Xs + kXTile;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2; ++s) {
       u32x4 xf[2], wf[4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
