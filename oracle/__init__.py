@@ -3,8 +3,8 @@
 Test infrastructure: only tests/, the smoke check and the bench's CPU-baseline
 leg may import this package. The product path never does.
 """
-from .attention_ref import (attention_ref, attention_weights_ref, causal_mask, causal_mask_rows, linear_ref,
+from .attention_ref import (attention_ref, attention_weights_ref, causal_mask, causal_mask_rows, key_padding_mask_row, linear_ref,
                             concat_heads, mha_ref, softmax_rows, split_heads)
 
-__all__ = ["attention_ref", "attention_weights_ref", "causal_mask", "causal_mask_rows",
+__all__ = ["attention_ref", "attention_weights_ref", "causal_mask", "causal_mask_rows", "key_padding_mask_row",
            "concat_heads", "linear_ref", "mha_ref", "softmax_rows", "split_heads"]

@@ -22,11 +22,17 @@ in float64, materialising the full score matrix:
   weight of exactly 0 -- "The Transformer" (rayaq.ca), "Masks: who may look at
   whom", with its printed 4x4 example.
 
+* A key-padding mask works the same way, one row per batch item: every key
+  at or past the item's length gets -inf for every query -- same page, same
+  section, on the *_key_padding_mask arguments. The length is given as a
+  number of valid keys, so no boolean polarity is involved.
+
 Readings where the pages are silent (each is listed in the design notes):
 the softmax subtracts the row maximum before exponentiating (softmax is
 unchanged by a per-row shift; it only avoids overflow); no biases in the
-projections; weights are stored (in, out) so Q = X W; the mask is only
-defined for N_q == N_k.
+projections; weights are stored (in, out) so Q = X W; the causal mask is only
+defined for N_q == N_k; a row whose keys are all masked (length 0) has no
+softmax, and its output is taken as 0 with a log-sum-exp of -inf.
 
 Every function here is pinned by tests/test_oracle.py against properties the
 pages fix (rows sum to 1, permutation equivariance, the printed mask, closed
@@ -87,13 +93,25 @@ def attention_weights_ref(q: np.ndarray, k: np.ndarray, *, causal: bool = False,
     return softmax_rows(s)
 
 
+def key_padding_mask_row(n_k: int, length: int) -> np.ndarray:
+    """Additive key-padding row of one batch item: 0 for keys j < length,
+    -inf for j >= length ("The Transformer" (rayaq.ca), "Masks: who may look
+    at whom": padding masks, one row per batch item)."""
+    m = np.zeros((n_k,), dtype=np.float64)
+    m[int(length):] = -np.inf
+    return m
+
+
 def attention_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool = False,
-                  scale: float | None = None, rows=None):
+                  scale: float | None = None, rows=None, kv_len=None):
     """O = softmax(scale * Q K^T (+ mask)) V over every (batch, head).
 
     q: (B, H, N_q, d_k), k: (B, H, N_k, d_k), v: (B, H, N_k, d_v); any float
     dtype, widened exactly to float64. rows: optional sorted query positions
     (the same for every (b, h)); the outputs then hold only those rows.
+    kv_len: optional per-batch number of valid keys (clamped to [0, N_k]);
+    keys at or past it are masked for every query and head of that item.
+    A row with no unmasked key gets O = 0, rowsum = 0 and lse = -inf.
 
     Returns (O, rowsum, lse):
       O      (B, H, R, d_v)  attention output
@@ -121,13 +139,19 @@ def attention_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool =
                 if n_q != k.shape[2]:
                     raise ValueError("the causal mask is defined for N_q == N_k only")
                 s = s + causal_mask_rows(k.shape[2], pos)
+            if kv_len is not None:
+                length = min(max(int(kv_len[b]), 0), k.shape[2])
+                s = s + key_padding_mask_row(k.shape[2], length)[None, :]
+            dead = np.all(s == -np.inf, axis=-1)       # rows with no unmasked key
+            s = np.where(dead[:, None], 0.0, s)         # placeholder, overwritten below
             m = np.max(s, axis=-1, keepdims=True)
             e = np.exp(s - m)
             l = np.sum(e, axis=-1, keepdims=True)
             p = e / l
+            p[dead] = 0.0
             o[b, h] = np.matmul(p, v[b, h])
             rowsum[b, h] = np.sum(p, axis=-1)
-            lse[b, h] = (m + np.log(l))[:, 0]
+            lse[b, h] = np.where(dead, -np.inf, (m + np.log(l))[:, 0])
     return o, rowsum, lse
 
 
@@ -158,7 +182,7 @@ def concat_heads(t: np.ndarray) -> np.ndarray:
 
 def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: np.ndarray,
             wv: np.ndarray, wo: np.ndarray, heads: int, *, causal: bool = False,
-            rows=None) -> np.ndarray:
+            rows=None, kv_len=None) -> np.ndarray:
     """MultiHead(Xq, Xk, Xv) = Concat(head_1..head_h) W^O, no biases.
 
     xq: (B, N_q, d_model); xk, xv: (B, N_k, d_model); w*: (d_model, d_model)
@@ -169,6 +193,8 @@ def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: 
     decoder state as xq and the encoder memory as xk and xv ("The Transformer"
     (rayaq.ca), "The decoder stack").
     rows: optional query positions; only those output rows are returned.
+    kv_len: optional per-batch number of valid key/value positions of the
+    xk/xv sequence (a key-padding mask, as in attention_ref).
     """
     xq = np.asarray(xq, dtype=np.float64)
     xk = np.asarray(xk, dtype=np.float64)
@@ -181,7 +207,7 @@ def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: 
     v = np.matmul(xv, np.asarray(wv, dtype=np.float64))
     qh, kh, vh = split_heads(q, heads), split_heads(k, heads), split_heads(v, heads)
     o, _, _ = attention_ref(qh, kh, vh, causal=causal, scale=1.0 / math.sqrt(d_model // heads),
-                            rows=rows)
+                            rows=rows, kv_len=kv_len)
     return np.matmul(concat_heads(o), np.asarray(wo, dtype=np.float64))
 
 

@@ -390,8 +390,86 @@ def check_lse(attn):
         assert np.allclose(lse, want, rtol=0, atol=1e-13), "lse"
 
 
+# ------------------------------------------------------------------ key-padding masks (per-batch key lengths)
+def check_key_padding(attn):
+    """A key-padding mask blocks, for every query of a batch item, the keys at
+    or past that item's length ("The Transformer" (rayaq.ca), "Masks: who may
+    look at whom": padding masks work like the causal one, one row per batch
+    item). Pinned by an independent route: the same item computed on keys
+    truncated to its length, unmasked."""
+    q, k, v = _qkv(41, B=4, H=2, nq=6, nk=9, d=4, dv=3)
+    lens = [9, 4, 1, 12]  # full, partial, one key, longer than N_k (clamped)
+    o, rs, lse = attn(q, k, v, kv_len=lens)
+    for b, L in enumerate(lens):
+        L = min(L, 9)
+        want, wrs, wlse = attn(q[b:b + 1], k[b:b + 1, :, :L], v[b:b + 1, :, :L])
+        assert np.allclose(o[b], want[0], rtol=0, atol=1e-14), f"padding of item {b} (length {L})"
+        assert np.allclose(lse[b], wlse[0], rtol=0, atol=1e-14), "lse under padding"
+        assert np.allclose(rs[b], 1.0, rtol=0, atol=1e-12)
+    # the padded keys and values are never read: changing them changes nothing, bitwise
+    k2, v2 = k.copy(), v.copy()
+    k2[1, :, 4:] = 1e3
+    v2[1, :, 4:] = -7.0
+    o2, _, _ = attn(q, k2, v2, kv_len=lens)
+    assert np.array_equal(o2, o), "a padded key or value leaked into the output"
+    # causal and padding together: row i sees keys j <= min(i, L - 1)
+    q, k, v = _qkv(42, B=2, H=1, nq=7, nk=7, d=3)
+    o, _, _ = attn(q, k, v, causal=True, kv_len=[7, 3])
+    full, _, _ = attn(q[1:], k[1:], v[1:], causal=True)
+    assert np.allclose(o[1, :, :3], full[0, :, :3], rtol=0, atol=1e-14), "causal rows inside the length"
+    trunc, _, _ = attn(q[1:, :, 3:], k[1:, :, :3], v[1:, :, :3])
+    assert np.allclose(o[1, :, 3:], trunc[0], rtol=0, atol=1e-14), "causal rows past the length see every valid key"
+    assert np.allclose(o[0], attn(q[:1], k[:1], v[:1], causal=True)[0][0], rtol=0, atol=1e-14)
+
+
+def check_fully_masked_rows(attn):
+    """A batch item with length 0 has no visible key. The pages define no
+    softmax for such a row; the reading adopted here: output 0, row sum 0,
+    log-sum-exp -inf (and the other items are unaffected)."""
+    q, k, v = _qkv(43, B=3, H=2, nq=4, nk=5, d=3)
+    for causal_ok in (False,):
+        o, rs, lse = attn(q, k, v, kv_len=[5, 0, 2])
+        assert np.array_equal(o[1], np.zeros_like(o[1])), "fully masked rows must give 0"
+        assert np.all(rs[1] == 0.0) and np.all(np.isneginf(lse[1])), "row sum 0, lse -inf"
+        assert np.all(np.isfinite(o)), "no NaN anywhere"
+        ref, _, _ = attn(q[:1], k[:1], v[:1])
+        assert np.allclose(o[0], ref[0], rtol=0, atol=1e-14)
+
+
+def check_torch_padding(attn, mha):
+    """torch's float64 scaled_dot_product_attention with a boolean attn_mask
+    (True = may attend) and nn.MultiheadAttention with key_padding_mask
+    (True = blocked): the two polarities the pages warn about ("Masks: who may
+    look at whom"; "Pitfalls"). Cross-check only."""
+    import torch
+    import torch.nn.functional as F
+    q, k, v = _qkv(44, B=3, H=2, nq=5, nk=8, d=4)
+    lens = [8, 3, 1]
+    o, _, _ = attn(q, k, v, kv_len=lens)
+    allow = torch.arange(8)[None, :] < torch.tensor(lens)[:, None]       # True = may attend
+    t = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                       attn_mask=allow[:, None, None, :])
+    assert np.allclose(o, t.numpy(), rtol=0, atol=1e-12), "differs from torch sdpa with a key mask"
+    r = _rng(45)
+    B, N, M, dm, h = 3, 4, 6, 8, 2
+    xq, xkv = r.standard_normal((B, N, dm)), r.standard_normal((B, M, dm))
+    wq, wk, wv, wo = (r.standard_normal((dm, dm)) for _ in range(4))
+    m = torch.nn.MultiheadAttention(dm, h, bias=False, batch_first=True).double()
+    with torch.no_grad():
+        m.in_proj_weight.copy_(torch.from_numpy(np.concatenate([wq.T, wk.T, wv.T])))
+        m.out_proj.weight.copy_(torch.from_numpy(wo.T))
+    m.eval()
+    lens = [6, 2, 5]
+    blocked = torch.arange(M)[None, :] >= torch.tensor(lens)[:, None]     # True = blocked
+    with torch.no_grad():
+        t, _ = m(torch.from_numpy(xq), torch.from_numpy(xkv), torch.from_numpy(xkv),
+                 key_padding_mask=blocked, need_weights=False)
+    got = mha(xq, xkv, xkv, wq, wk, wv, wo, h, kv_len=lens)
+    assert np.allclose(got, t.numpy(), rtol=0, atol=1e-12), "differs from nn.MultiheadAttention with padding"
+
+
 ATTENTION_PINS = [check_rows_sum_to_one, check_permutation_equivariance,
                   check_constant_v_and_convex_hull, check_causal_locality,
                   check_masked_weight_is_zero, check_closed_forms, check_low_temperature_argmax,
                   check_default_scale, check_brute_force, check_hand_example,
-                  check_linearity_and_shift, check_lse]
+                  check_linearity_and_shift, check_lse, check_key_padding, check_fully_masked_rows]

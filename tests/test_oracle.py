@@ -52,6 +52,17 @@ def test_torch_cross_check():
     pins.check_torch_sdpa(oracle.attention_ref, oracle.mha_ref)
 
 
+def test_torch_padding_cross_check():
+    pins.check_torch_padding(oracle.attention_ref, oracle.mha_ref)
+
+
+def test_padding_row_is_the_printed_form():
+    # one row per batch item, 0 where the key may be read and -inf past the length
+    row = oracle.key_padding_mask_row(5, 3)
+    assert np.array_equal(row[:3], np.zeros(3)) and np.all(np.isneginf(row[3:]))
+    assert np.array_equal(oracle.key_padding_mask_row(4, 0), np.full(4, -np.inf))
+
+
 def test_causal_rejects_cross_shapes():
     r = np.random.default_rng(4)
     q, k = r.standard_normal((1, 1, 3, 2)), r.standard_normal((1, 1, 5, 2))

@@ -15,7 +15,7 @@ from tests import oracle_pins as pins
 
 
 def _mutant_attention(mutation):
-    def attn(q, k, v, *, causal=False, scale=None, rows=None):
+    def attn(q, k, v, *, causal=False, scale=None, rows=None, kv_len=None):
         q = np.asarray(q, np.float64)
         k = np.asarray(k, np.float64)
         v = np.asarray(v, np.float64)
@@ -43,6 +43,15 @@ def _mutant_attention(mutation):
                         pass
                     else:
                         s = np.where(blocked, -np.inf, s)
+                if kv_len is not None:
+                    L = min(max(int(kv_len[b]), 0), nk)
+                    j = np.arange(nk)[None, :]
+                    pad = {"pad_keeps_one_more": j > L, "pad_polarity": j < L,
+                           "pad_on_queries": np.zeros((1, nk), bool)}.get(mutation, j >= L)
+                    s = np.where(pad, -np.inf, s)
+                dead = np.all(s == -np.inf, axis=-1)
+                if mutation != "pad_dead_rows_nan":
+                    s = np.where(dead[:, None], 0.0, s)
                 axis = -2 if mutation == "softmax_wrong_axis" else -1
                 m = np.max(s, axis=axis, keepdims=True)
                 e = np.exp(s - m)
@@ -50,19 +59,26 @@ def _mutant_attention(mutation):
                 p = e if mutation == "no_normalise" else e / l
                 if causal and mutation == "mask_after_softmax":
                     p = np.where(np.arange(nk)[None, :] > pos[:, None], 0.0, p)
+                if mutation != "pad_dead_rows_nan":
+                    p[dead] = 0.0
                 vv = kk[:, :v.shape[-1]] if mutation == "uses_k_for_v" else v[b, h]
                 if mutation == "transposed_p" and p.shape[0] == p.shape[1]:
                     p = p.T
                 o[b, h] = p @ vv
+                if mutation == "pad_on_queries" and kv_len is not None:
+                    o[b, h][pos >= min(max(int(kv_len[b]), 0), nk)] = 0.0
                 rs[b, h] = p.sum(-1)
                 lse[b, h] = (m + np.log(l))[:, 0] if axis == -1 else np.log(np.exp(s).sum(-1))
+                if mutation != "pad_dead_rows_nan":
+                    lse[b, h] = np.where(dead, -np.inf, lse[b, h])
         return o, rs, lse
     return attn
 
 
 ATTENTION_MUTANTS = ["scale_times_sqrt_d", "no_scale", "scale_one_over_d", "sign_flip",
                      "mask_flipped", "mask_no_diagonal", "mask_off_by_one", "mask_after_softmax",
-                     "softmax_wrong_axis", "no_normalise", "uses_k_for_v", "transposed_p"]
+                     "softmax_wrong_axis", "no_normalise", "uses_k_for_v", "transposed_p",
+                     "pad_keeps_one_more", "pad_polarity", "pad_on_queries", "pad_dead_rows_nan"]
 
 
 def _caught(fn):
@@ -85,7 +101,7 @@ def test_attention_mutant_is_caught(mutation):
 
 
 def _mutant_mha(mutation):
-    def mha(xq, xk, xv, wq, wk, wv, wo, heads, *, causal=False, rows=None):
+    def mha(xq, xk, xv, wq, wk, wv, wo, heads, *, causal=False, rows=None, kv_len=None):
         xq, xk, xv = (np.asarray(t, np.float64) for t in (xq, xk, xv))
         wq, wk, wv, wo = (np.asarray(t, np.float64) for t in (wq, wk, wv, wo))
         if mutation == "weights_transposed":
@@ -102,7 +118,8 @@ def _mutant_mha(mutation):
         q, k, v = split(xq @ wq), split(xk @ wk), split(xv @ wv)
         if mutation == "value_from_query_input":
             v = split(xq @ wv)
-        o, _, _ = oracle.attention_ref(q, k, v, causal=causal, scale=1 / math.sqrt(d), rows=rows)
+        o, _, _ = oracle.attention_ref(q, k, v, causal=causal, scale=1 / math.sqrt(d), rows=rows,
+                                       kv_len=None if mutation == "padding_dropped" else kv_len)
         if mutation == "concat_reversed":
             o = o[:, ::-1]
         cat = o.transpose(0, 2, 1, 3).reshape(B, o.shape[2], dm)
@@ -113,7 +130,7 @@ def _mutant_mha(mutation):
 
 
 MHA_MUTANTS = ["weights_transposed", "heads_interleaved", "concat_reversed",
-               "no_output_projection", "value_from_query_input"]
+               "no_output_projection", "value_from_query_input", "padding_dropped"]
 
 
 @pytest.mark.parametrize("mutation", MHA_MUTANTS)
@@ -121,6 +138,7 @@ def test_mha_mutant_is_caught(mutation):
     mha = _mutant_mha(mutation)
     checks = [lambda: pins.check_mha_structure(mha, oracle.attention_ref),
               lambda: pins.check_torch_sdpa(oracle.attention_ref, mha),
+              lambda: pins.check_torch_padding(oracle.attention_ref, mha),
               lambda: pins.check_parameter_counts(mha)]
     assert any(_caught(c) for c in checks), f"no pin catches the mutant {mutation!r}"
 
@@ -133,3 +151,4 @@ def test_unmutated_copies_pass():
     mha = _mutant_mha("none")
     pins.check_mha_structure(mha, oracle.attention_ref)
     pins.check_torch_sdpa(oracle.attention_ref, mha)
+    pins.check_torch_padding(oracle.attention_ref, mha)
