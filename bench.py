@@ -106,7 +106,7 @@ def cpu_baseline(w, inputs, min_seconds=10.0, max_seconds=30.0):
     if w.kind == "mha":
         xv = inputs["x"].value
         args = (xv, xv, xv, inputs["wq"].value, inputs["wk"].value, inputs["wv"].value, inputs["wo"].value)
-        fn = lambda: oracle.mha_ref(*args, w.heads, causal=w.causal)
+        fn = lambda: oracle.mha_ref(*args, w.heads, causal=w.causal, kv_len=w.kv_lengths())
         flops = w.total_flops()
         sample = f"the full workload ({w.batch} batch elements), oracle.mha_ref in float64"
     else:
@@ -139,7 +139,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="encoder", help="encoder | tiny | decoder | cross | long")
+    ap.add_argument("--workload", default="encoder", help="encoder | tiny | decoder | cross | long | padded")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the long causal attention line")
     ap.add_argument("--calib-copy", action="store_true",
@@ -164,6 +164,8 @@ def main():
     inputs = workloads.make_inputs(w)
 
     result = {}
+    lens = w.kv_lengths()
+    kv_len = None if lens is None else torch.from_numpy(lens).to(dev)
     if w.kind == "mha":
         dm = w.d_model
         x = torch_tensor(inputs["x"], dev)
@@ -178,7 +180,8 @@ def main():
 
         def step(i):
             xi = xs[i % n_sets]
-            mha.mha_forward(xi, xi, xi, *ws, w.heads, causal=w.causal, out=outs[i % n_sets], workspace=work)
+            mha.mha_forward(xi, xi, xi, *ws, w.heads, causal=w.causal, out=outs[i % n_sets], workspace=work,
+                            kv_len=kv_len)
 
         # parity on the exact launch configuration that is timed
         step(0)
@@ -193,10 +196,12 @@ def main():
         off_v = off_k + (B * w.n_k * dm * esz + 255) // 256 * 256
         vv = work[off_v:off_v + B * w.n_k * dm * esz].view(x.dtype).view(B, w.n_k, H, d).transpose(1, 2)
         ov = torch.empty((B, N, H, d), dtype=x.dtype, device=dev).transpose(1, 2)
-        dom_fn = lambda i: mha.attention_forward(qv, kv, vv, causal=w.causal, out=ov)
+        dom_fn = lambda i: mha.attention_forward(qv, kv, vv, causal=w.causal, out=ov, kv_len=kv_len)
         dom_flops = w.attention_flops()
         dom_name = "attn_fwd_bf16_d64" if w.dtype == "bf16" else "attn_fwd_f32"
-        dom_bytes = 2 * (B * H * N * d + 2 * B * H * w.n_k * d + B * H * N * d) * (esz // 2)
+        # Q in, O out; K and V only over the visible keys
+        kv_rows = B * w.n_k if lens is None else int(lens.astype(np.int64).sum())
+        dom_bytes = 2 * (B * H * N * d + 2 * H * kv_rows * d + B * H * N * d) * (esz // 2)
         get_out = lambda: outs[0]
     else:
         q, k, v = (torch_tensor(inputs[n], dev) for n in ("q", "k", "v"))
@@ -279,6 +284,9 @@ def main():
            "step": "mha_forward: QKV projections + attention + W^O" if w.kind == "mha" else "attention_forward"}
     if w.kind == "mha":
         cfg["d_model"] = w.d_model
+    if lens is not None:
+        cfg["kv_len"] = (f"per-batch key lengths uniform in [{w.kv_len_range[0]}, {w.kv_len_range[1]}] "
+                         f"(seeded; mean {float(lens.mean()):.1f})")
     line = {"metric": "attention fwd TFLOP/s and % of bf16 MFMA peak at 1 GPU (h=8, d_k=64)",
             "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",

@@ -14,6 +14,10 @@
  *   Causal mask: key j is blocked for query i when j > i (diagonal kept), by
  *     adding -inf to the score before the softmax, so blocked keys weigh
  *     exactly 0 -- "The Transformer" (rayaq.ca), "Masks: who may look at whom".
+ *   Key-padding mask: keys at or past a batch item's length are blocked for
+ *     every query of that item the same way -- same section (padding masks,
+ *     one row per batch item). Given as a number of valid keys per item, so
+ *     there is no boolean polarity to get wrong.
  *
  * Conventions shared by every entry point
  *   - Every data pointer is DEVICE memory owned by the caller. The library
@@ -88,6 +92,28 @@ mha_status attention_forward(const void* q, const void* k, const void* v, void* 
                              void* stream);
 
 /*
+ * attention_forward_padded -- attention_forward with a key-padding mask.
+ *
+ * kv_len: DEVICE pointer to `batch` int32 values, 4-byte aligned, owned by the
+ *   caller and read by the kernels (not on the host). Key j is blocked for
+ *   every query and head of batch item b when j >= kv_len[b]; values are
+ *   clamped to [0, n_k]. Combined with causal = 1, query i sees keys
+ *   j <= min(i, kv_len[b] - 1).
+ * A row with no visible key (kv_len[b] == 0) has no softmax: its output is 0
+ *   and its lse is -inf (the pages leave such rows undefined).
+ * Every other argument, rule and status is that of attention_forward; a NULL
+ *   kv_len is MHA_ERR_INVALID_ARG (call attention_forward instead).
+ * Work and traffic shrink with the lengths: key tiles past kv_len[b] are
+ *   never loaded.
+ */
+mha_status attention_forward_padded(const void* q, const void* k, const void* v, void* o,
+                                    int batch, int heads, int n_q, int n_k, int d_k, int d_v,
+                                    const int64_t q_strides[3], const int64_t k_strides[3],
+                                    const int64_t v_strides[3], const int64_t o_strides[3],
+                                    mha_dtype dtype, int causal, float scale, const int32_t* kv_len,
+                                    float* lse, void* stream);
+
+/*
  * linear_forward -- one projection, Y = X W (no bias), the building block of
  * the Q/K/V projections and of W^O ("The Transformer" (hoshank.vercel.app),
  * "The Mathematics": W_i^Q etc. are d_model x d_k matrices applied on the
@@ -136,6 +162,22 @@ mha_status mha_forward(const void* xq, const void* xk, const void* xv, const voi
                        const void* wk, const void* wv, const void* wo, void* out,
                        void* workspace, size_t workspace_bytes, int batch, int n_q, int n_k,
                        int d_model, int heads, mha_dtype dtype, int causal, void* stream);
+
+/*
+ * mha_forward_padded -- mha_forward with a key-padding mask on the xk/xv
+ * sequence (encoder self-attention over a padded batch, or cross-attention to
+ * a padded encoder memory; "The Transformer" (rayaq.ca), "Masks: who may look
+ * at whom"). kv_len is as in attention_forward_padded: a device array of
+ * `batch` int32 key lengths, clamped to [0, n_k]. Output rows of an item with
+ * length 0 are 0 W^O = 0. A NULL kv_len is MHA_ERR_INVALID_ARG.
+ * The projections still run over all n_k rows; only the attention skips the
+ * padded keys.
+ */
+mha_status mha_forward_padded(const void* xq, const void* xk, const void* xv, const void* wq,
+                              const void* wk, const void* wv, const void* wo, void* out,
+                              void* workspace, size_t workspace_bytes, int batch, int n_q, int n_k,
+                              int d_model, int heads, mha_dtype dtype, int causal,
+                              const int32_t* kv_len, void* stream);
 
 /* Static English name of a status code (never NULL). */
 const char* mha_status_string(mha_status status);

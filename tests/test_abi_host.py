@@ -34,8 +34,9 @@ def lib():
 
 def test_header_declares_the_boundary():
     fns = header_functions()
-    assert {"attention_forward", "mha_forward", "mha_forward_workspace_size", "linear_forward",
-            "mha_status_string", "mha_last_error", "mha_version"} == set(fns)
+    assert {"attention_forward", "attention_forward_padded", "mha_forward", "mha_forward_padded",
+            "mha_forward_workspace_size", "linear_forward", "mha_status_string", "mha_last_error",
+            "mha_version"} == set(fns)
     assert set(fns) == set(_lib.SIGNATURES), "binding signatures out of sync with include/mha.h"
 
 
@@ -85,6 +86,38 @@ def test_attention_validation(lib, kw, status, needle):
 
 def test_misaligned_lse_rejected(lib):
     assert attn(lib, lse=MIS) == _lib.MHA_ERR_INVALID_ARG
+
+
+def attn_padded(lib, kv_len=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=2, H=8, nq=64, nk=64, dk=64, dv=64, qs=S_BHND, ks=S_BHND,
+             vs=S_BHND, os_=S_BHND, dtype=_lib.MHA_BF16, causal=0, scale=0.125, lse=None)
+    a.update(kw)
+    return lib.attention_forward_padded(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["nq"], a["nk"], a["dk"],
+                                        a["dv"], _lib.strides3(a["qs"]), _lib.strides3(a["ks"]),
+                                        _lib.strides3(a["vs"]), _lib.strides3(a["os_"]), a["dtype"], a["causal"],
+                                        a["scale"], kv_len, a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(kv_len=None), _lib.MHA_ERR_INVALID_ARG, "kv_len"),
+    (dict(kv_len=FAKE + 2), _lib.MHA_ERR_INVALID_ARG, "kv_len"),
+    (dict(q=None), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(causal=1, nq=64, nk=65), _lib.MHA_ERR_INVALID_ARG, "n_q == n_k"),
+    (dict(dk=32, dv=32), _lib.MHA_ERR_UNSUPPORTED, "d_k = 64"),
+])
+def test_padded_attention_validation(lib, kw, status, needle):
+    """The padded entry point checks its own argument, then applies every
+    rule of attention_forward."""
+    assert attn_padded(lib, **kw) == status
+    assert needle in lib.mha_last_error().decode()
+
+
+def test_padded_mha_validation(lib):
+    assert lib.mha_forward_padded(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 2, 16, 16, 512, 8,
+                                  _lib.MHA_BF16, 0, None, None) == _lib.MHA_ERR_INVALID_ARG
+    assert "kv_len" in lib.mha_last_error().decode()
+    assert lib.mha_forward_padded(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 2, 16, 16, 512, 8,
+                                  _lib.MHA_BF16, 0, FAKE, None) == _lib.MHA_ERR_WORKSPACE
 
 
 def test_null_stride_array_rejected(lib):

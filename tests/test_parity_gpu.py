@@ -290,3 +290,75 @@ def test_binding_reports_workspace_error(dev):
     small = torch.empty(16, dtype=torch.uint8, device=dev)
     with pytest.raises(mha.MHAError, match="MHA_ERR_WORKSPACE"):
         mha.mha_forward(x["x"], x["x"], x["x"], x["wq"], x["wk"], x["wv"], x["wo"], 8, workspace=small)
+
+
+# ---------------------------------------------------------------- key-padding masks (per-batch key lengths)
+PADDED = [
+    # (B, H, n_q, n_k, causal, dtype, lengths)
+    (4, 2, 100, 130, False, "bf16", [130, 65, 0, 1]),
+    (3, 2, 129, 129, True, "bf16", [129, 64, 200]),
+    (2, 3, 2600, 2600, True, "bf16", [2600, 1000]),
+    (2, 1, 2100, 2300, False, "bf16", [0, 2299]),
+    (3, 2, 70, 90, False, "f32", [90, 33, 0]),
+    (2, 2, 65, 65, True, "f32", [65, 7]),
+]
+
+
+@pytest.mark.parametrize("B,H,nq,nk,causal,dtype,lens", PADDED)
+def test_padded_attention_parity(dev, B, H, nq, nk, causal, dtype, lens):
+    import torch
+    q = workloads.random_tensor((B, H, nq, 64), dtype, seed=500 + nq)
+    k = workloads.random_tensor((B, H, nk, 64), dtype, seed=600 + nk)
+    v = workloads.random_tensor((B, H, nk, 64), dtype, seed=700 + nk)
+    kv_len = torch.tensor(lens, dtype=torch.int32, device=dev)
+    say(f"padded {B}x{H} nq={nq} nk={nk} causal={causal} {dtype} lens={lens}")
+    o, lse = mha.attention_forward(to_device(q, dev), to_device(k, dev), to_device(v, dev), causal=causal,
+                                   kv_len=kv_len, return_lse=True)
+    torch.cuda.synchronize()
+    want, _, want_lse = oracle.attention_ref(q.value, k.value, v.value, causal=causal, kv_len=lens)
+    assert_close(to_f64(o), want, dtype, "padded attention")
+    got_lse = to_f64(lse)
+    dead = np.isneginf(want_lse)
+    assert np.array_equal(np.isneginf(got_lse), dead), "rows with no visible key must report lse = -inf"
+    assert max_abs(got_lse[~dead], want_lse[~dead]) <= LSE_TOL[dtype], "log-sum-exp under padding"
+
+
+def test_padded_keys_are_never_read(dev):
+    """Changing K and V past a batch item's length leaves the output bitwise unchanged."""
+    import torch
+    B, H, n = 2, 2, 300
+    q, k, v = (to_device(workloads.random_tensor((B, H, n, 64), "bf16", seed=800 + i), dev) for i in range(3))
+    kv_len = torch.tensor([300, 111], dtype=torch.int32, device=dev)
+    say("padded keys never read")
+    a = mha.attention_forward(q, k, v, kv_len=kv_len)
+    k2, v2 = k.clone(), v.clone()
+    k2[1, :, 111:] = 30.0
+    v2[1, :, 111:] = float("nan")
+    b = mha.attention_forward(q, k2, v2, kv_len=kv_len)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_padded_mha_parity(dev, dtype):
+    import torch
+    B, nq, nk, dm, h = 3, 40, 75, 512 if dtype == "bf16" else 256, 8 if dtype == "bf16" else 4
+    xq = workloads.random_tensor((B, nq, dm), dtype, seed=901)
+    mem = workloads.random_tensor((B, nk, dm), dtype, seed=902)
+    ws = [workloads.random_tensor((dm, dm), dtype, seed=903 + i, scale=1 / math.sqrt(dm)) for i in range(4)]
+    tw = [to_device(s, dev) for s in ws]
+    lens = [75, 20, 0]
+    kv_len = torch.tensor(lens, dtype=torch.int32, device=dev)
+    say(f"padded mha cross {dtype}")
+    out = mha.mha_forward(to_device(xq, dev), to_device(mem, dev), to_device(mem, dev), *tw, h, kv_len=kv_len)
+    torch.cuda.synchronize()
+    want = oracle.mha_ref(xq.value, mem.value, mem.value, *[s.value for s in ws], h, kv_len=lens)
+    assert_close(to_f64(out), want, dtype, "padded mha cross")
+    assert float(out[2].abs().max()) == 0.0, "an item with no visible key gives 0 W^O = 0"
+    say(f"padded mha causal self {dtype}")
+    xs = workloads.random_tensor((B, nk, dm), dtype, seed=910)
+    t = to_device(xs, dev)
+    out = mha.mha_forward(t, t, t, *tw, h, causal=True, kv_len=kv_len)
+    torch.cuda.synchronize()
+    want = oracle.mha_ref(xs.value, xs.value, xs.value, *[s.value for s in ws], h, causal=True, kv_len=lens)
+    assert_close(to_f64(out), want, dtype, "padded mha causal")

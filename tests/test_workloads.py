@@ -46,3 +46,23 @@ def test_sample_rows():
     assert len(rows) == 64 == len(set(rows.tolist()))
     assert set(workloads.EDGE_ROWS) <= set(rows.tolist())
     assert np.all(np.diff(rows) > 0) and rows.max() < w.n_q
+
+
+def test_padded_workload_lengths_and_pairs():
+    w = workloads.get("padded")
+    lens = w.kv_lengths()
+    assert lens.dtype == np.int32 and lens.shape == (32,)
+    assert np.array_equal(lens, w.kv_lengths())
+    assert lens.min() >= 64 and lens.max() <= 512
+    assert w.total_pairs() == int(np.sum(lens)) * w.n_q
+    assert w.attention_flops() == 4 * 8 * 64 * w.total_pairs()
+    # the causal count under padding equals a brute-force count of visible (i, j)
+    import dataclasses
+    c = dataclasses.replace(w, causal=True, n_q=40, n_k=40, kv_len_range=(0, 40))
+    want = 0
+    for L in c.kv_lengths():
+        i = np.arange(40)[:, None]
+        j = np.arange(40)[None, :]
+        want += int(np.sum((j <= i) & (j < L)))
+    assert c.total_pairs() == want
+    assert workloads.get("encoder").kv_lengths() is None

@@ -49,14 +49,29 @@ def _stream_handle(dev, stream):
     return s.cuda_stream
 
 
+def _kv_len_arg(kv_len, B, dev):
+    """Check a key-length tensor: int32, on the device, (B,) contiguous."""
+    torch = _torch()
+    if not isinstance(kv_len, torch.Tensor) or kv_len.dtype != torch.int32:
+        raise TypeError("kv_len must be an int32 tensor of per-batch key lengths")
+    if not kv_len.is_cuda or kv_len.device != dev:
+        raise ValueError("kv_len must live on the same GPU as the inputs")
+    if tuple(kv_len.shape) != (B,) or not kv_len.is_contiguous():
+        raise ValueError(f"kv_len must be a contiguous ({B},) tensor")
+    return kv_len.data_ptr()
+
+
 def attention_forward(q, k, v, *, causal: bool = False, scale: float | None = None, out=None,
-                      return_lse: bool = False, stream=None):
+                      return_lse: bool = False, kv_len=None, stream=None):
     """O = softmax(scale * Q K^T (+ causal mask)) V for (batch, heads, n, d) tensors.
 
     q: (B, H, N_q, d), k: (B, H, N_k, d), v: (B, H, N_k, d); any strides with a
     contiguous last dimension (so (B, N, H, d) buffers can be passed through
     .transpose(1, 2) without a copy). Returns out (B, H, N_q, d), and the fp32
     log-sum-exp (B, H, N_q) when return_lse is set.
+    kv_len: optional int32 device tensor (B,) of key lengths (a key-padding
+    mask): keys at or past kv_len[b] are blocked for batch item b; a row with
+    no visible key returns 0 (lse -inf). Calls attention_forward_padded.
     """
     torch = _torch()
     dev = _require_device(q, k, v)
@@ -77,11 +92,15 @@ def attention_forward(q, k, v, *, causal: bool = False, scale: float | None = No
         scale = 1.0 / math.sqrt(d_k)
     lib = load()
     with torch.cuda.device(dev):
-        st = lib.attention_forward(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, n_q, n_k, d_k, d_v,
-            strides3(q.stride()[:3]), strides3(k.stride()[:3]), strides3(v.stride()[:3]),
-            strides3(out.stride()[:3]), _dtype_code(q), int(bool(causal)), float(scale),
-            lse.data_ptr() if lse is not None else None, _stream_handle(dev, stream))
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, n_q, n_k, d_k, d_v,
+                strides3(q.stride()[:3]), strides3(k.stride()[:3]), strides3(v.stride()[:3]),
+                strides3(out.stride()[:3]), _dtype_code(q), int(bool(causal)), float(scale))
+        lse_p = lse.data_ptr() if lse is not None else None
+        if kv_len is None:
+            st = lib.attention_forward(*args, lse_p, _stream_handle(dev, stream))
+        else:
+            st = lib.attention_forward_padded(*args, _kv_len_arg(kv_len, B, dev), lse_p,
+                                              _stream_handle(dev, stream))
     check(st)
     return (out, lse) if return_lse else out
 
@@ -116,12 +135,14 @@ def mha_forward_workspace_size(batch: int, n_q: int, n_k: int, d_model: int, hea
 
 
 def mha_forward(xq, xk, xv, wq, wk, wv, wo, heads: int, *, causal: bool = False, out=None,
-                workspace=None, stream=None):
+                workspace=None, kv_len=None, stream=None):
     """MultiHead(xq, xk, xv) = Concat(head_1..head_h) W^O, bias-free.
 
     xq (B, N_q, d_model); xk, xv (B, N_k, d_model); w* (d_model, d_model) stored
     (in, out). Pass the same tensor three times for self-attention. workspace,
     if given, is a uint8 device tensor of at least mha_forward_workspace_size bytes.
+    kv_len: optional int32 device tensor (B,) of key lengths of the xk/xv
+    sequence (a key-padding mask); calls mha_forward_padded.
     """
     torch = _torch()
     dev = _require_device(xq, xk, xv, wq, wk, wv, wo)
@@ -145,9 +166,13 @@ def mha_forward(xq, xk, xv, wq, wk, wv, wo, heads: int, *, causal: bool = False,
     if tuple(out.shape) != (B, n_q, d_model) or not out.is_contiguous():
         raise ValueError("out must be a contiguous (B, N_q, d_model) tensor")
     with torch.cuda.device(dev):
-        st = lib.mha_forward(xq.data_ptr(), xk.data_ptr(), xv.data_ptr(), wq.data_ptr(), wk.data_ptr(),
-                             wv.data_ptr(), wo.data_ptr(), out.data_ptr(), workspace.data_ptr(),
-                             workspace.numel() * workspace.element_size(), B, n_q, n_k, d_model, heads,
-                             code, int(bool(causal)), _stream_handle(dev, stream))
+        args = (xq.data_ptr(), xk.data_ptr(), xv.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+                wv.data_ptr(), wo.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), B, n_q, n_k, d_model, heads,
+                code, int(bool(causal)))
+        if kv_len is None:
+            st = lib.mha_forward(*args, _stream_handle(dev, stream))
+        else:
+            st = lib.mha_forward_padded(*args, _kv_len_arg(kv_len, B, dev), _stream_handle(dev, stream))
     check(st)
     return out

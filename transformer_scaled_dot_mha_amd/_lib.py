@@ -23,11 +23,16 @@ SIGNATURES = {
     "attention_forward": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int,
                                  _i64x3, _i64x3, _i64x3, _i64x3, _int, _int, ctypes.c_float,
                                  _vp, _vp]),
+    "attention_forward_padded": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int,
+                                        _i64x3, _i64x3, _i64x3, _i64x3, _int, _int, ctypes.c_float,
+                                        _vp, _vp, _vp]),
     "linear_forward": (_int, [_vp, _vp, _vp, _int, _int, _int, ctypes.c_int64, ctypes.c_int64,
                               ctypes.c_int64, _int, _vp]),
     "mha_forward_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int, _int, _int]),
     "mha_forward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                            _int, _int, _int, _int, _int, _int, _int, _vp]),
+    "mha_forward_padded": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                  _int, _int, _int, _int, _int, _int, _int, _vp, _vp]),
     "mha_status_string": (ctypes.c_char_p, [_int]),
     "mha_last_error": (ctypes.c_char_p, []),
     "mha_version": (_int, []),

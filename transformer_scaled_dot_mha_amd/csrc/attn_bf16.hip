@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
   const int lane = tid & 63;
   const int lq = lane & 31;
   const int hf = lane >> 5;
-  const int n_q = a.n_q, n_k = a.n_k;
+  const int n_q = a.n_q;
 
   // ---- workgroup -> (batch*head, query block)
   int bh, qblk;
@@ -363,6 +363,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
     qblk = logical - bh * n_qblk;
   }
   const int b = bh / a.heads, h = bh - b * a.heads;
+  // keys visible to this batch item: all n_k, or its padded length
+  const int n_k = a.kv_len != nullptr ? min(max(a.kv_len[b], 0), a.n_k) : a.n_k;
   const bf16* qp = static_cast<const bf16*>(a.q) + b * a.q_sb + h * a.q_sh;
   const bf16* kp = static_cast<const bf16*>(a.k) + b * a.k_sb + h * a.k_sh;
   const bf16* vp = static_cast<const bf16*>(a.v) + b * a.v_sb + h * a.v_sh;
@@ -400,11 +402,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
                         (int)(((int64_t)(v_key + 1) * a.v_sn + 8 * v_chunk) * 2)};
   u32x4 kreg[2], vreg[2];
   auto gload = [&](int k0) {
+    // record counts end at the last visible key row (none when no key is visible)
     const int valid = min(n_k - k0, kBN);
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kp + (int64_t)k0 * a.k_sn), (short)0, (int)((valid - 1) * a.k_sn * 2 + 2 * 64), kBufferFlags);
+        (void*)(kp + (int64_t)k0 * a.k_sn), (short)0, valid > 0 ? (int)((valid - 1) * a.k_sn * 2 + 2 * 64) : 0,
+        kBufferFlags);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vp + (int64_t)k0 * a.v_sn), (short)0, (int)((valid - 1) * a.v_sn * 2 + 2 * 64), kBufferFlags);
+        (void*)(vp + (int64_t)k0 * a.v_sn), (short)0, valid > 0 ? (int)((valid - 1) * a.v_sn * 2 + 2 * 64) : 0,
+        kBufferFlags);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off[i], 0, 0));
@@ -476,7 +481,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
   for (int qb = 0; qb < kQB; ++qb) {
     const int my_q = q_wave0 + 32 * qb + lq;
     const float l_tot = sum_halves(st[qb].l);
-    const float inv = 1.0f / l_tot;
+    // a row with no visible key (padded length 0) has l = 0: output 0, lse -inf
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     unsigned w[2][4][2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -499,7 +505,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
           *reinterpret_cast<u32x4*>(dst + 32 * blk + 8 * (2 * tt + hf)) = chunk[blk][tt];
-      if (a.lse != nullptr && hf == 0) a.lse[(int64_t)bh * n_q + my_q] = (st[qb].mc + __log2f(l_tot)) * kLn2;
+      if (a.lse != nullptr && hf == 0)
+        a.lse[(int64_t)bh * n_q + my_q] = l_tot > 0.f ? (st[qb].mc + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }

@@ -30,7 +30,9 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32(AttnArgs a, float c, float
   const float* kp = static_cast<const float*>(a.k) + b * a.k_sb + h * a.k_sh;
   const float* vp = static_cast<const float*>(a.v) + b * a.v_sb + h * a.v_sh;
   float* op = static_cast<float*>(a.o) + b * a.o_sb + h * a.o_sh;
-  const int n_q = a.n_q, n_k = a.n_k;
+  const int n_q = a.n_q;
+  // keys visible to this batch item: all n_k, or its padded length
+  const int n_k = a.kv_len != nullptr ? min(max(a.kv_len[b], 0), a.n_k) : a.n_k;
   const int my_q = qb * kRows + tid;
 
   float qr[D], acc[D];
@@ -79,11 +81,13 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32(AttnArgs a, float c, float
     }
   }
   if (my_q < n_q) {
-    const float inv = 1.0f / l_run;
+    // a row with no visible key (padded length 0) has l = 0: output 0, lse -inf
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
     float* dst = op + (int64_t)my_q * a.o_sn;
 #pragma unroll
     for (int t = 0; t < D; ++t) dst[t] = acc[t] * inv;
-    if (a.lse != nullptr) a.lse[(int64_t)bh * n_q + my_q] = m_run * (c / 1.4426950408889634f) + logf(l_run);
+    if (a.lse != nullptr)
+      a.lse[(int64_t)bh * n_q + my_q] = l_run > 0.f ? m_run * (c / 1.4426950408889634f) + logf(l_run) : -INFINITY;
   }
 }
 

@@ -14,6 +14,9 @@ struct AttnArgs {
   const void* v;
   void* o;
   float* lse;  // nullable, (batch, heads, n_q) contiguous
+  // nullable, device (batch) int32: keys at or past kv_len[b] are masked for
+  // batch item b (clamped to [0, n_k] in the kernels)
+  const int* kv_len;
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;

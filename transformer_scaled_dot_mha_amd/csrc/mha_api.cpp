@@ -34,6 +34,7 @@ mha_status hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Element multiple that keeps every 16-byte vector access aligned.
 int vec_elems(mha_dtype t) { return t == MHA_BF16 ? 8 : 4; }
@@ -109,8 +110,8 @@ mha_status validate_attention(const void* q, const void* k, const void* v, void*
   return MHA_OK;
 }
 
-mha::AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
-                        int heads, int n_q, int n_k, int d, const int64_t* qs, const int64_t* ks,
+mha::AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, float* lse, const int* kv_len,
+                        int batch, int heads, int n_q, int n_k, int d, const int64_t* qs, const int64_t* ks,
                         const int64_t* vs, const int64_t* os, int causal, float scale) {
   mha::AttnArgs a;
   a.q = q;
@@ -118,6 +119,7 @@ mha::AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, fl
   a.v = v;
   a.o = o;
   a.lse = lse;
+  a.kv_len = kv_len;
   a.q_sb = qs[0], a.q_sh = qs[1], a.q_sn = qs[2];
   a.k_sb = ks[0], a.k_sh = ks[1], a.k_sn = ks[2];
   a.v_sb = vs[0], a.v_sh = vs[1], a.v_sn = vs[2];
@@ -161,6 +163,88 @@ mha_status run_linear(const mha::LinearArgs& a, mha_dtype dtype, hipStream_t str
   return hip_status(e, "projection launch");
 }
 
+mha_status attention_impl(const void* q, const void* k, const void* v, void* o, int batch, int heads, int n_q,
+                          int n_k, int d_k, int d_v, const int64_t* q_strides, const int64_t* k_strides,
+                          const int64_t* v_strides, const int64_t* o_strides, mha_dtype dtype, int causal, float scale,
+                          const int32_t* kv_len, float* lse, void* stream) {
+  mha_status s = validate_attention(q, k, v, o, batch, heads, n_q, n_k, d_k, d_v, q_strides, k_strides, v_strides,
+                                    o_strides, (int)dtype, causal, scale);
+  if (s != MHA_OK) return s;
+  if (lse && !aligned16(lse)) return fail(MHA_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+  const mha::AttnArgs a = attn_args(q, k, v, o, lse, kv_len, batch, heads, n_q, n_k, d_k, q_strides, k_strides,
+                                    v_strides, o_strides, causal, scale);
+  return run_attention(a, dtype, static_cast<hipStream_t>(stream));
+}
+
+mha_status mha_impl(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk, const void* wv,
+                    const void* wo, void* out, void* workspace, size_t workspace_bytes, int batch, int n_q, int n_k,
+                    int d_model, int heads, mha_dtype dtype, int causal, const int32_t* kv_len, void* stream) {
+  if (!xq || !xk || !xv || !wq || !wk || !wv || !wo || !out)
+    return fail(MHA_ERR_INVALID_ARG, "inputs, weights and out must be non-null");
+  if (!workspace) return fail(MHA_ERR_INVALID_ARG, "workspace must be non-null");
+  if (batch < 1 || n_q < 1 || n_k < 1 || d_model < 1 || heads < 1)
+    return fail(MHA_ERR_INVALID_ARG, "sizes must be >= 1 (batch=%d n_q=%d n_k=%d d_model=%d heads=%d)", batch,
+                n_q, n_k, d_model, heads);
+  if (!valid_dtype((int)dtype)) return fail(MHA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (d_model % heads)
+    return fail(MHA_ERR_INVALID_ARG, "d_model (%d) must be divisible by heads (%d)", d_model, heads);
+  if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (causal && n_q != n_k)
+    return fail(MHA_ERR_INVALID_ARG, "the causal mask is defined for n_q == n_k (got %d and %d)", n_q, n_k);
+  if (d_model > kMaxLdX) return fail(MHA_ERR_UNSUPPORTED, "d_model (%d) too large, at most %lld", d_model, (long long)kMaxLdX);
+  const int d = d_model / heads;
+  mha_status s = check_head_width(dtype, d, d);
+  if (s != MHA_OK) return s;
+  const void* ptrs[9] = {xq, xk, xv, wq, wk, wv, wo, out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(MHA_ERR_INVALID_ARG, "every pointer must be 16-byte aligned");
+  WsLayout w;
+  if (!ws_layout(batch, n_q, n_k, d_model, dtype, &w))
+    return fail(MHA_ERR_UNSUPPORTED, "workspace size overflows");
+  if (workspace_bytes < w.total)
+    return fail(MHA_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.total);
+  const int64_t rows_q = (int64_t)batch * n_q, rows_k = (int64_t)batch * n_k;
+  if (rows_q > INT32_MAX || rows_k > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "batch * sequence too large");
+  if ((int64_t)batch * heads * ((n_q + 63) / 64) > INT32_MAX)
+    return fail(MHA_ERR_UNSUPPORTED, "too many (batch, head, query block) triples");
+
+  char* ws = static_cast<char*>(workspace);
+  void* qw = ws + w.q;
+  void* kw = ws + w.k;
+  void* vw = ws + w.v;
+  void* ow = ws + w.o;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // (1) Q, K, V projections in one grouped launch; row-major (rows, d_model)
+  //     is already the head-split (batch, n, heads, d) layout.
+  mha::LinearArgs lin = {};
+  lin.g[0] = mha::LinearGroup{xq, wq, qw, (int)rows_q, d_model, d_model, d_model};
+  lin.g[1] = mha::LinearGroup{xk, wk, kw, (int)rows_k, d_model, d_model, d_model};
+  lin.g[2] = mha::LinearGroup{xv, wv, vw, (int)rows_k, d_model, d_model, d_model};
+  lin.groups = 3;
+  lin.n = d_model;
+  lin.k = d_model;
+  s = run_linear(lin, dtype, st);
+  if (s != MHA_OK) return s;
+
+  // (2) attention over the strided head views; the output lands directly in
+  //     the concatenated (batch, n_q, heads * d) layout.
+  const int64_t qs[3] = {(int64_t)n_q * d_model, d, d_model};
+  const int64_t kvs[3] = {(int64_t)n_k * d_model, d, d_model};
+  const mha::AttnArgs a = attn_args(qw, kw, vw, ow, nullptr, kv_len, batch, heads, n_q, n_k, d, qs, kvs, kvs, qs,
+                                    causal, 1.0f / sqrtf((float)d));
+  s = run_attention(a, dtype, st);
+  if (s != MHA_OK) return s;
+
+  // (3) output projection W^O
+  mha::LinearArgs out_lin = {};
+  out_lin.g[0] = mha::LinearGroup{ow, wo, out, (int)rows_q, d_model, d_model, d_model};
+  out_lin.groups = 1;
+  out_lin.n = d_model;
+  out_lin.k = d_model;
+  return run_linear(out_lin, dtype, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,7 +262,7 @@ const char* mha_status_string(mha_status s) {
 
 const char* mha_last_error(void) { return g_last_error.c_str(); }
 
-int mha_version(void) { return 100; }
+int mha_version(void) { return 200; }
 
 mha_status attention_forward(const void* q, const void* k, const void* v, void* o, int batch, int heads,
                              int n_q, int n_k, int d_k, int d_v, const int64_t q_strides[3],
@@ -186,15 +270,25 @@ mha_status attention_forward(const void* q, const void* k, const void* v, void* 
                              const int64_t o_strides[3], mha_dtype dtype, int causal, float scale, float* lse,
                              void* stream) {
   try {
-    mha_status s = validate_attention(q, k, v, o, batch, heads, n_q, n_k, d_k, d_v, q_strides, k_strides,
-                                      v_strides, o_strides, (int)dtype, causal, scale);
-    if (s != MHA_OK) return s;
-    if (lse && !aligned16(lse)) return fail(MHA_ERR_INVALID_ARG, "lse must be 16-byte aligned");
-    const mha::AttnArgs a = attn_args(q, k, v, o, lse, batch, heads, n_q, n_k, d_k, q_strides, k_strides,
-                                      v_strides, o_strides, causal, scale);
-    return run_attention(a, dtype, static_cast<hipStream_t>(stream));
+    return attention_impl(q, k, v, o, batch, heads, n_q, n_k, d_k, d_v, q_strides, k_strides, v_strides, o_strides,
+                          dtype, causal, scale, nullptr, lse, stream);
   } catch (...) {
     return fail(MHA_ERR_HIP, "internal error in attention_forward");
+  }
+}
+
+mha_status attention_forward_padded(const void* q, const void* k, const void* v, void* o, int batch, int heads,
+                                    int n_q, int n_k, int d_k, int d_v, const int64_t q_strides[3],
+                                    const int64_t k_strides[3], const int64_t v_strides[3],
+                                    const int64_t o_strides[3], mha_dtype dtype, int causal, float scale,
+                                    const int32_t* kv_len, float* lse, void* stream) {
+  try {
+    if (!kv_len) return fail(MHA_ERR_INVALID_ARG, "kv_len must be non-null (use attention_forward for no padding)");
+    if (!aligned4(kv_len)) return fail(MHA_ERR_INVALID_ARG, "kv_len must be 4-byte aligned");
+    return attention_impl(q, k, v, o, batch, heads, n_q, n_k, d_k, d_v, q_strides, k_strides, v_strides, o_strides,
+                          dtype, causal, scale, kv_len, lse, stream);
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in attention_forward_padded");
   }
 }
 
@@ -226,72 +320,24 @@ mha_status mha_forward(const void* xq, const void* xk, const void* xv, const voi
                        int batch, int n_q, int n_k, int d_model, int heads, mha_dtype dtype, int causal,
                        void* stream) {
   try {
-    if (!xq || !xk || !xv || !wq || !wk || !wv || !wo || !out)
-      return fail(MHA_ERR_INVALID_ARG, "inputs, weights and out must be non-null");
-    if (!workspace) return fail(MHA_ERR_INVALID_ARG, "workspace must be non-null");
-    if (batch < 1 || n_q < 1 || n_k < 1 || d_model < 1 || heads < 1)
-      return fail(MHA_ERR_INVALID_ARG, "sizes must be >= 1 (batch=%d n_q=%d n_k=%d d_model=%d heads=%d)", batch,
-                  n_q, n_k, d_model, heads);
-    if (!valid_dtype((int)dtype)) return fail(MHA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-    if (d_model % heads)
-      return fail(MHA_ERR_INVALID_ARG, "d_model (%d) must be divisible by heads (%d)", d_model, heads);
-    if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
-    if (causal && n_q != n_k)
-      return fail(MHA_ERR_INVALID_ARG, "the causal mask is defined for n_q == n_k (got %d and %d)", n_q, n_k);
-    if (d_model > kMaxLdX) return fail(MHA_ERR_UNSUPPORTED, "d_model (%d) too large, at most %lld", d_model, (long long)kMaxLdX);
-    const int d = d_model / heads;
-    mha_status s = check_head_width(dtype, d, d);
-    if (s != MHA_OK) return s;
-    const void* ptrs[9] = {xq, xk, xv, wq, wk, wv, wo, out, workspace};
-    for (const void* p : ptrs)
-      if (!aligned16(p)) return fail(MHA_ERR_INVALID_ARG, "every pointer must be 16-byte aligned");
-    WsLayout w;
-    if (!ws_layout(batch, n_q, n_k, d_model, dtype, &w))
-      return fail(MHA_ERR_UNSUPPORTED, "workspace size overflows");
-    if (workspace_bytes < w.total)
-      return fail(MHA_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, w.total);
-    const int64_t rows_q = (int64_t)batch * n_q, rows_k = (int64_t)batch * n_k;
-    if (rows_q > INT32_MAX || rows_k > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "batch * sequence too large");
-    if ((int64_t)batch * heads * ((n_q + 63) / 64) > INT32_MAX)
-      return fail(MHA_ERR_UNSUPPORTED, "too many (batch, head, query block) triples");
-
-    char* ws = static_cast<char*>(workspace);
-    void* qw = ws + w.q;
-    void* kw = ws + w.k;
-    void* vw = ws + w.v;
-    void* ow = ws + w.o;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-
-    // (1) Q, K, V projections in one grouped launch; row-major (rows, d_model)
-    //     is already the head-split (batch, n, heads, d) layout.
-    mha::LinearArgs lin = {};
-    lin.g[0] = mha::LinearGroup{xq, wq, qw, (int)rows_q, d_model, d_model, d_model};
-    lin.g[1] = mha::LinearGroup{xk, wk, kw, (int)rows_k, d_model, d_model, d_model};
-    lin.g[2] = mha::LinearGroup{xv, wv, vw, (int)rows_k, d_model, d_model, d_model};
-    lin.groups = 3;
-    lin.n = d_model;
-    lin.k = d_model;
-    s = run_linear(lin, dtype, st);
-    if (s != MHA_OK) return s;
-
-    // (2) attention over the strided head views; the output lands directly in
-    //     the concatenated (batch, n_q, heads * d) layout.
-    const int64_t qs[3] = {(int64_t)n_q * d_model, d, d_model};
-    const int64_t kvs[3] = {(int64_t)n_k * d_model, d, d_model};
-    const mha::AttnArgs a = attn_args(qw, kw, vw, ow, nullptr, batch, heads, n_q, n_k, d, qs, kvs, kvs, qs,
-                                      causal, 1.0f / sqrtf((float)d));
-    s = run_attention(a, dtype, st);
-    if (s != MHA_OK) return s;
-
-    // (3) output projection W^O
-    mha::LinearArgs out_lin = {};
-    out_lin.g[0] = mha::LinearGroup{ow, wo, out, (int)rows_q, d_model, d_model, d_model};
-    out_lin.groups = 1;
-    out_lin.n = d_model;
-    out_lin.k = d_model;
-    return run_linear(out_lin, dtype, st);
+    return mha_impl(xq, xk, xv, wq, wk, wv, wo, out, workspace, workspace_bytes, batch, n_q, n_k, d_model, heads,
+                    dtype, causal, nullptr, stream);
   } catch (...) {
     return fail(MHA_ERR_HIP, "internal error in mha_forward");
+  }
+}
+
+mha_status mha_forward_padded(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk,
+                              const void* wv, const void* wo, void* out, void* workspace, size_t workspace_bytes,
+                              int batch, int n_q, int n_k, int d_model, int heads, mha_dtype dtype, int causal,
+                              const int32_t* kv_len, void* stream) {
+  try {
+    if (!kv_len) return fail(MHA_ERR_INVALID_ARG, "kv_len must be non-null (use mha_forward for no padding)");
+    if (!aligned4(kv_len)) return fail(MHA_ERR_INVALID_ARG, "kv_len must be 4-byte aligned");
+    return mha_impl(xq, xk, xv, wq, wk, wv, wo, out, workspace, workspace_bytes, batch, n_q, n_k, d_model, heads,
+                    dtype, causal, kv_len, stream);
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in mha_forward_padded");
   }
 }
 

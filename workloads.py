@@ -40,20 +40,45 @@ class Workload:
     seed: int
     d_model: int = 0     # mha workloads only
     oracle_rows: int = 0  # >0: the oracle checks this many sampled query positions
+    kv_len_range: tuple = ()  # (lo, hi): per-batch key lengths drawn uniformly in [lo, hi] (padding mask)
+
+    def kv_lengths(self):
+        """Per-batch key lengths of a padded workload (None if unpadded), from
+        their own generator ``default_rng(2000 + seed)`` so that the tensors'
+        draws do not depend on them."""
+        if not self.kv_len_range:
+            return None
+        lo, hi = self.kv_len_range
+        return np.random.default_rng(2000 + self.seed).integers(lo, hi + 1, size=self.batch).astype(np.int32)
 
     @property
     def d_v(self) -> int:
         return self.d_k
 
     def attention_pairs(self) -> int:
-        """Unmasked (query, key) pairs per (batch, head)."""
-        if self.causal:
-            return self.n_q * (self.n_q + 1) // 2
-        return self.n_q * self.n_k
+        """Unmasked (query, key) pairs per (batch, head); for a padded workload,
+        the mean over the batch items of their own counts times the batch
+        (attention_flops uses the exact total)."""
+        return self.total_pairs() // self.batch
+
+    def total_pairs(self) -> int:
+        """Unmasked (query, key) pairs summed over the batch, per head."""
+        lens = self.kv_lengths()
+        if lens is None:
+            lens = np.full(self.batch, self.n_k)
+        tot = 0
+        for L in lens:
+            L = int(min(max(L, 0), self.n_k))
+            if self.causal:
+                # query i sees keys j <= min(i, L - 1)
+                tot += L * (L + 1) // 2 + (self.n_q - L) * L if L <= self.n_q else self.n_q * (self.n_q + 1) // 2
+            else:
+                tot += self.n_q * L
+        return tot
 
     def attention_flops(self) -> int:
-        """4 * B * H * d * pairs: QK^T and PV, two flops per multiply-add."""
-        return 4 * self.batch * self.heads * self.d_k * self.attention_pairs()
+        """4 * H * d * (unmasked pairs over the batch): QK^T and PV, two flops per multiply-add."""
+        return 4 * self.heads * self.d_k * self.total_pairs()
 
     def projection_flops(self) -> int:
         if self.kind != "mha":
@@ -81,6 +106,9 @@ WORKLOADS: dict[str, Workload] = {
                  n_q=384, n_k=512, d_k=64, causal=False, seed=4),
         Workload("long_causal_bf16_b2_h16_n8192", "attn", "bf16", batch=2, heads=16,
                  n_q=8192, n_k=8192, d_k=64, causal=True, seed=5, oracle_rows=64),
+        # the base encoder over a padded batch: key lengths uniform in [64, 512]
+        Workload("base_encoder_padded_mha_bf16_b32_n512", "mha", "bf16", batch=32, heads=8,
+                 n_q=512, n_k=512, d_k=64, causal=False, seed=6, d_model=512, kv_len_range=(64, 512)),
     ]
 }
 
@@ -91,6 +119,7 @@ ALIASES = {
     "decoder": "decoder_causal_bf16_b16_h8_n1024",
     "cross": "cross_attn_bf16_b32_h8_nq384_nk512",
     "long": "long_causal_bf16_b2_h16_n8192",
+    "padded": "base_encoder_padded_mha_bf16_b32_n512",
 }
 
 
