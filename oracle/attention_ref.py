@@ -182,7 +182,7 @@ def concat_heads(t: np.ndarray) -> np.ndarray:
 
 def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: np.ndarray,
             wv: np.ndarray, wo: np.ndarray, heads: int, *, causal: bool = False,
-            rows=None, kv_len=None) -> np.ndarray:
+            rows=None, kv_len=None, bq=None, bk=None, bv=None, bo=None) -> np.ndarray:
     """MultiHead(Xq, Xk, Xv) = Concat(head_1..head_h) W^O, no biases.
 
     xq: (B, N_q, d_model); xk, xv: (B, N_k, d_model); w*: (d_model, d_model)
@@ -195,6 +195,10 @@ def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: 
     rows: optional query positions; only those output rows are returned.
     kv_len: optional per-batch number of valid key/value positions of the
     xk/xv sequence (a key-padding mask, as in attention_ref).
+    bq, bk, bv, bo: optional biases (d_model,) added after each projection, as
+    in the encoder layer's attention module ("The Transformer" (rayaq.ca), "In
+    PyTorch": nn.MultiheadAttention, whose parameters the printed count
+    includes). The MultiHead equation itself has none.
     """
     xq = np.asarray(xq, dtype=np.float64)
     xk = np.asarray(xk, dtype=np.float64)
@@ -202,13 +206,57 @@ def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: 
     d_model = xq.shape[-1]
     if d_model % heads:
         raise ValueError("d_model must be divisible by the number of heads")
-    q = np.matmul(xq, np.asarray(wq, dtype=np.float64))
-    k = np.matmul(xk, np.asarray(wk, dtype=np.float64))
-    v = np.matmul(xv, np.asarray(wv, dtype=np.float64))
+    def proj(x, w, b):
+        y = np.matmul(x, np.asarray(w, dtype=np.float64))
+        return y if b is None else y + np.asarray(b, dtype=np.float64)
+
+    q, k, v = proj(xq, wq, bq), proj(xk, wk, bk), proj(xv, wv, bv)
     qh, kh, vh = split_heads(q, heads), split_heads(k, heads), split_heads(v, heads)
     o, _, _ = attention_ref(qh, kh, vh, causal=causal, scale=1.0 / math.sqrt(d_model // heads),
                             rows=rows, kv_len=kv_len)
-    return np.matmul(concat_heads(o), np.asarray(wo, dtype=np.float64))
+    return proj(concat_heads(o), wo, bo)
+
+
+def layer_norm_ref(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float) -> np.ndarray:
+    """LayerNorm over the last axis: each position's d_model numbers are
+    shifted to mean 0 and scaled to variance 1 (the population variance, the
+    mean of squared deviations), then scaled by gamma and shifted by beta
+    ("The Transformer" (rayaq.ca), "Residuals and LayerNorm"). eps is added to
+    the variance under the square root; the pages print no value (reading in
+    the design notes: 1e-5, the default of the nn.LayerNorm their code uses)."""
+    x = np.asarray(x, dtype=np.float64)
+    mean = np.mean(x, axis=-1, keepdims=True)
+    var = np.mean((x - mean) ** 2, axis=-1, keepdims=True)
+    return (x - mean) / np.sqrt(var + eps) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+
+
+def ffn_ref(x: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray, b2: np.ndarray) -> np.ndarray:
+    """Position-wise feed-forward network FFN(x) = max(0, x W1 + b1) W2 + b2,
+    widening d_model -> d_ff and back ("The Transformer" (hoshank.vercel.app),
+    "The Mathematics", the FFN equation and its symbol table). Weights (in, out)."""
+    x = np.asarray(x, dtype=np.float64)
+    h = np.maximum(0.0, np.matmul(x, np.asarray(w1, np.float64)) + np.asarray(b1, np.float64))
+    return np.matmul(h, np.asarray(w2, np.float64)) + np.asarray(b2, np.float64)
+
+
+def encoder_layer_ref(x: np.ndarray, p: dict, heads: int, *, eps: float = 1e-5, causal: bool = False,
+                      kv_len=None) -> np.ndarray:
+    """One encoder layer, post-norm: h = LayerNorm(x + MHA(x)), then
+    out = LayerNorm(h + FFN(h)) ("The Transformer" (hoshank.vercel.app), "The
+    Mathematics": output = LayerNorm(x + Sublayer(x)) around both sub-layers;
+    "The Transformer" (rayaq.ca), "In PyTorch", the EncoderLayer forward, in
+    eval mode, so without dropout).
+
+    p holds wq, wk, wv, wo, bq, bk, bv, bo (attention), ln1_g, ln1_b, w1, b1,
+    w2, b2, ln2_g, ln2_b, all (in, out). kv_len: optional key-padding lengths
+    for the self-attention, as in attention_ref.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = mha_ref(x, x, x, p["wq"], p["wk"], p["wv"], p["wo"], heads, causal=causal, kv_len=kv_len,
+                bq=p["bq"], bk=p["bk"], bv=p["bv"], bo=p["bo"])
+    h = layer_norm_ref(x + a, p["ln1_g"], p["ln1_b"], eps)
+    f = ffn_ref(h, p["w1"], p["b1"], p["w2"], p["b2"])
+    return layer_norm_ref(h + f, p["ln2_g"], p["ln2_b"], eps)
 
 
 def linear_ref(x: np.ndarray, w: np.ndarray) -> np.ndarray:

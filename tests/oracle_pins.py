@@ -468,6 +468,119 @@ def check_torch_padding(attn, mha):
     assert np.allclose(got, t.numpy(), rtol=0, atol=1e-12), "differs from nn.MultiheadAttention with padding"
 
 
+# ------------------------------------------------------------------ encoder sub-layer (LayerNorm, FFN, residuals)
+def encoder_params(seed, d, ff, scale=1.0):
+    """Random encoder-layer parameters in the oracle's (in, out) layout."""
+    r = _rng(seed)
+    p = {n: r.standard_normal((d, d)) / math.sqrt(d) * scale for n in ("wq", "wk", "wv", "wo")}
+    p.update({n: r.standard_normal(d) * 0.1 for n in ("bq", "bk", "bv", "bo")})
+    p["w1"] = r.standard_normal((d, ff)) / math.sqrt(d)
+    p["b1"] = r.standard_normal(ff) * 0.1
+    p["w2"] = r.standard_normal((ff, d)) / math.sqrt(ff)
+    p["b2"] = r.standard_normal(d) * 0.1
+    for n in ("ln1", "ln2"):
+        p[n + "_g"] = 1.0 + 0.1 * r.standard_normal(d)
+        p[n + "_b"] = 0.1 * r.standard_normal(d)
+    return p
+
+
+def check_layer_norm(ln):
+    """Each position's numbers are shifted to mean 0 and scaled to variance 1
+    (population variance), then scaled and shifted ("The Transformer"
+    (rayaq.ca), "Residuals and LayerNorm")."""
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    eps = 1e-5
+    want = (x - 2.5) / math.sqrt(1.25 + eps)         # mean 2.5, mean squared deviation 1.25
+    assert np.allclose(ln(x, np.ones(4), np.zeros(4), eps), want, rtol=0, atol=1e-15), "hand example"
+    r = _rng(50)
+    x = r.standard_normal((3, 5, 64)) * 3.0 + 2.0
+    y = ln(x, np.ones(64), np.zeros(64), 0.0)
+    assert np.allclose(y.mean(-1), 0.0, atol=1e-13) and np.allclose((y ** 2).mean(-1), 1.0, atol=1e-12)
+    g, b = r.standard_normal(64), r.standard_normal(64)
+    assert np.allclose(ln(x, g, b, eps), ln(x, np.ones(64), np.zeros(64), eps) * g + b, rtol=0, atol=1e-12)
+    # per-row shift and positive scale do not change it (eps = 0)
+    assert np.allclose(ln(5.0 * x - 7.0, np.ones(64), np.zeros(64), 0.0), y, rtol=0, atol=1e-12)
+
+
+def check_ffn(ffn):
+    """FFN(x) = max(0, x W1 + b1) W2 + b2 ("The Transformer" (hoshank.vercel.app),
+    "The Mathematics"), by hand on integers, one token at a time."""
+    x = np.array([[1.0, -2.0], [0.0, 3.0]])
+    w1 = np.array([[1.0, 0.0, -1.0], [2.0, 1.0, 0.0]])
+    b1 = np.array([0.0, 1.0, 0.5])
+    w2 = np.array([[1.0], [-1.0], [2.0]])
+    b2 = np.array([0.25])
+    want = []
+    for t in x:  # position-wise: each token alone
+        hid = [max(0.0, sum(t[i] * w1[i, j] for i in range(2)) + b1[j]) for j in range(3)]
+        want.append([sum(hid[j] * w2[j, 0] for j in range(3)) + b2[0]])
+    assert np.allclose(ffn(x, w1, b1, w2, b2), np.array(want), rtol=0, atol=1e-15), "FFN by hand"
+
+
+def check_encoder_layer_torch(layer):
+    """torch's float64 nn.TransformerEncoderLayer (post-norm, ReLU, eval mode,
+    batch_first) with the same parameters computes the same layer ("The
+    Transformer" (rayaq.ca), "In PyTorch" and "Residuals and LayerNorm").
+    Cross-check only; also with a key-padding mask (True = blocked) and with
+    the causal mask."""
+    import torch
+    d, h, ff = 16, 2, 32
+    p = encoder_params(51, d, ff)
+    m = torch.nn.TransformerEncoderLayer(d, h, dim_feedforward=ff, dropout=0.0, batch_first=True).double().eval()
+    with torch.no_grad():
+        m.self_attn.in_proj_weight.copy_(torch.from_numpy(np.concatenate([p["wq"].T, p["wk"].T, p["wv"].T])))
+        m.self_attn.in_proj_bias.copy_(torch.from_numpy(np.concatenate([p["bq"], p["bk"], p["bv"]])))
+        m.self_attn.out_proj.weight.copy_(torch.from_numpy(p["wo"].T))
+        m.self_attn.out_proj.bias.copy_(torch.from_numpy(p["bo"]))
+        m.linear1.weight.copy_(torch.from_numpy(p["w1"].T))
+        m.linear1.bias.copy_(torch.from_numpy(p["b1"]))
+        m.linear2.weight.copy_(torch.from_numpy(p["w2"].T))
+        m.linear2.bias.copy_(torch.from_numpy(p["b2"]))
+        m.norm1.weight.copy_(torch.from_numpy(p["ln1_g"]))
+        m.norm1.bias.copy_(torch.from_numpy(p["ln1_b"]))
+        m.norm2.weight.copy_(torch.from_numpy(p["ln2_g"]))
+        m.norm2.bias.copy_(torch.from_numpy(p["ln2_b"]))
+    assert m.norm1.eps == 1e-5
+    x = _rng(52).standard_normal((3, 7, d))
+    with torch.no_grad():
+        t = m(torch.from_numpy(x)).numpy()
+    assert np.allclose(layer(x, p, h), t, rtol=0, atol=1e-12), "differs from nn.TransformerEncoderLayer"
+    lens = [7, 3, 5]
+    blocked = torch.arange(7)[None, :] >= torch.tensor(lens)[:, None]
+    with torch.no_grad():
+        t = m(torch.from_numpy(x), src_key_padding_mask=blocked).numpy()
+    assert np.allclose(layer(x, p, h, kv_len=lens), t, rtol=0, atol=1e-12), "padding mask"
+    causal = torch.triu(torch.full((7, 7), float("-inf"), dtype=torch.float64), diagonal=1)
+    with torch.no_grad():
+        t = m(torch.from_numpy(x), src_mask=causal).numpy()
+    assert np.allclose(layer(x, p, h, causal=True), t, rtol=0, atol=1e-12), "causal mask"
+
+
+def check_encoder_layer_structure(layer, ln, ffn, mha):
+    """The layer is the two wrapped sub-layers in order, post-norm: with the
+    attention output projection zeroed (W^O = 0, b^O = 0) the first sub-layer is
+    LayerNorm(x); with W2 = 0 and b2 = 0 the second is LayerNorm(h)."""
+    d, h, ff = 8, 2, 16
+    p = encoder_params(53, d, ff)
+    x = _rng(54).standard_normal((2, 5, d))
+    q = dict(p, wo=np.zeros((d, d)), bo=np.zeros(d), w2=np.zeros((ff, d)), b2=np.zeros(d))
+    want = ln(ln(x, p["ln1_g"], p["ln1_b"], 1e-5), p["ln2_g"], p["ln2_b"], 1e-5)
+    assert np.allclose(layer(x, q, h), want, rtol=0, atol=1e-12), "residual + post-norm order"
+    a = mha(x, x, x, p["wq"], p["wk"], p["wv"], p["wo"], h, bq=p["bq"], bk=p["bk"], bv=p["bv"], bo=p["bo"])
+    hh = ln(x + a, p["ln1_g"], p["ln1_b"], 1e-5)
+    want = ln(hh + ffn(hh, p["w1"], p["b1"], p["w2"], p["b2"]), p["ln2_g"], p["ln2_b"], 1e-5)
+    assert np.allclose(layer(x, p, h), want, rtol=0, atol=1e-13)
+
+
+def check_encoder_layer_params():
+    """The layer's parameters, in the shapes this build takes them, number
+    3,152,384 at the base size: the count printed on "The Transformer"
+    (rayaq.ca), "In PyTorch" (tests/golden/model_sizes.txt)."""
+    sizes = read_golden_table("model_sizes.txt")
+    p = encoder_params(55, sizes["base_d_model"], sizes["ffn_inner"])
+    assert sum(v.size for v in p.values()) == sizes["encoder_layer_params"]
+
+
 ATTENTION_PINS = [check_rows_sum_to_one, check_permutation_equivariance,
                   check_constant_v_and_convex_hull, check_causal_locality,
                   check_masked_weight_is_zero, check_closed_forms, check_low_temperature_argmax,

@@ -83,3 +83,24 @@ def test_linear_is_the_projection_used_by_mha():
     a, b = r.standard_normal((3, 5)), r.standard_normal((5, 2))
     y = oracle.linear_ref(a, b)
     assert abs(y[2, 1] - sum(a[2, t] * b[t, 1] for t in range(5))) < 1e-13
+
+
+def test_layer_norm():
+    pins.check_layer_norm(oracle.layer_norm_ref)
+
+
+def test_ffn():
+    pins.check_ffn(oracle.ffn_ref)
+
+
+def test_encoder_layer_against_torch():
+    pins.check_encoder_layer_torch(oracle.encoder_layer_ref)
+
+
+def test_encoder_layer_structure():
+    pins.check_encoder_layer_structure(oracle.encoder_layer_ref, oracle.layer_norm_ref, oracle.ffn_ref,
+                                       oracle.mha_ref)
+
+
+def test_encoder_layer_params():
+    pins.check_encoder_layer_params()

@@ -152,3 +152,60 @@ def test_unmutated_copies_pass():
     pins.check_mha_structure(mha, oracle.attention_ref)
     pins.check_torch_sdpa(oracle.attention_ref, mha)
     pins.check_torch_padding(oracle.attention_ref, mha)
+
+
+def _mutant_layer(mutation):
+    """The encoder layer with one planted mistake, built from the oracle's own
+    attention (already pinned above)."""
+    def ln(x, g, b, eps):
+        x = np.asarray(x, np.float64)
+        mu = x.mean(-1, keepdims=True)
+        dev = x - mu
+        n = x.shape[-1] - (1 if mutation == "unbiased_variance" else 0)
+        var = (dev ** 2).sum(-1, keepdims=True) / n
+        e = 0.0 if mutation == "no_eps" else eps
+        if mutation == "gamma_beta_swapped":
+            g, b = b, g
+        return dev / np.sqrt(var + e) * g + b
+
+    def ffn(x, w1, b1, w2, b2):
+        pre = x @ w1 + (0.0 if mutation == "ffn_bias_dropped" else b1)
+        hid = pre if mutation == "no_relu" else np.maximum(0.0, pre)
+        return hid @ w2 + b2
+
+    def layer(x, p, heads, *, eps=1e-5, causal=False, kv_len=None):
+        x = np.asarray(x, np.float64)
+        biases = {} if mutation == "attention_biases_dropped" else dict(bq=p["bq"], bk=p["bk"], bv=p["bv"],
+                                                                          bo=p["bo"])
+        def attn(t):
+            return oracle.mha_ref(t, t, t, p["wq"], p["wk"], p["wv"], p["wo"], heads, causal=causal,
+                                  kv_len=kv_len, **biases)
+        if mutation == "pre_norm":
+            h = x + attn(ln(x, p["ln1_g"], p["ln1_b"], eps))
+            return h + ffn(ln(h, p["ln2_g"], p["ln2_b"], eps), p["w1"], p["b1"], p["w2"], p["b2"])
+        a = attn(x)
+        h = ln(a if mutation == "no_residual" else x + a, p["ln1_g"], p["ln1_b"], eps)
+        f = ffn(h, p["w1"], p["b1"], p["w2"], p["b2"])
+        return ln(h + f, p["ln2_g"], p["ln2_b"], eps)
+    return layer, ln, ffn
+
+
+LAYER_MUTANTS = ["pre_norm", "no_residual", "unbiased_variance", "no_eps", "gamma_beta_swapped",
+                 "ffn_bias_dropped", "no_relu", "attention_biases_dropped"]
+
+
+@pytest.mark.parametrize("mutation", LAYER_MUTANTS)
+def test_layer_mutant_is_caught(mutation):
+    layer, ln, ffn = _mutant_layer(mutation)
+    checks = [lambda: pins.check_layer_norm(ln), lambda: pins.check_ffn(ffn),
+              lambda: pins.check_encoder_layer_torch(layer),
+              lambda: pins.check_encoder_layer_structure(layer, ln, ffn, oracle.mha_ref)]
+    assert any(_caught(c) for c in checks), f"no pin catches the mutant {mutation!r}"
+
+
+def test_unmutated_layer_passes():
+    layer, ln, ffn = _mutant_layer("none")
+    pins.check_layer_norm(ln)
+    pins.check_ffn(ffn)
+    pins.check_encoder_layer_torch(layer)
+    pins.check_encoder_layer_structure(layer, ln, ffn, oracle.mha_ref)
