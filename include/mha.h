@@ -179,6 +179,62 @@ mha_status mha_forward_padded(const void* xq, const void* xk, const void* xv, co
                               int d_model, int heads, mha_dtype dtype, int causal,
                               const int32_t* kv_len, void* stream);
 
+/*
+ * encoder_layer_forward -- one Transformer encoder layer, post-norm, inference:
+ *   h   = LayerNorm(x + MultiHead(x, x, x))            (attention with biases)
+ *   out = LayerNorm(h + FFN(h)),  FFN(h) = max(0, h W1 + b1) W2 + b2
+ *   -- "The Transformer" (hoshank.vercel.app), "The Mathematics": the FFN
+ *   equation and output = LayerNorm(x + Sublayer(x)) around both sub-layers;
+ *   "The Transformer" (rayaq.ca), "Residuals and LayerNorm" and "In PyTorch"
+ *   (the EncoderLayer forward in eval mode: no dropout).
+ * LayerNorm: per position, subtract the mean, divide by sqrt(population
+ *   variance + eps), then multiply by gamma and add beta. The pages print no
+ *   eps; 1e-5 is the default of the module their code uses.
+ * x, out: (batch, n, d_model) contiguous, of `dtype`. `weights` is a HOST
+ *   pointer to a struct of DEVICE pointers, every one non-null, 16-byte
+ *   aligned, of `dtype`, stored (in, out):
+ *     wq, wk, wv, wo (d_model, d_model); bq, bk, bv, bo (d_model);
+ *     ln1_gamma, ln1_beta (d_model); w1 (d_model, d_ff); b1 (d_ff);
+ *     w2 (d_ff, d_model); b2 (d_model); ln2_gamma, ln2_beta (d_model).
+ * workspace: device memory of at least encoder_layer_workspace_size() bytes;
+ *   scratch owned by the caller.
+ * causal, kv_len: masks of the self-attention, as in mha_forward and
+ *   mha_forward_padded (kv_len may be NULL: no padding).
+ * bf16: every stored tensor (the sub-layer outputs, h, the FFN hidden layer,
+ *   out) is rounded to bf16; the residual sums, the LayerNorm statistics and
+ *   every accumulation are fp32.
+ * Limits: d_model/heads follows attention_forward's head-width rules;
+ *   d_model and d_ff multiples of 8 (bf16) or 4 (f32); d_model <= 4096
+ *   (MHA_ERR_UNSUPPORTED above); eps finite and >= 0.
+ * Launches, all on `stream`: Q/K/V projections, attention, W^O, residual +
+ *   LayerNorm, W1 with bias and ReLU, W2 with bias, residual + LayerNorm.
+ */
+typedef struct mha_encoder_weights {
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+  const void* bq;
+  const void* bk;
+  const void* bv;
+  const void* bo;
+  const void* ln1_gamma;
+  const void* ln1_beta;
+  const void* w1;
+  const void* b1;
+  const void* w2;
+  const void* b2;
+  const void* ln2_gamma;
+  const void* ln2_beta;
+} mha_encoder_weights;
+
+size_t encoder_layer_workspace_size(int batch, int n, int d_model, int heads, int d_ff, mha_dtype dtype);
+
+mha_status encoder_layer_forward(const void* x, const mha_encoder_weights* weights, void* out,
+                                 void* workspace, size_t workspace_bytes, int batch, int n, int d_model,
+                                 int heads, int d_ff, float eps, mha_dtype dtype, int causal,
+                                 const int32_t* kv_len, void* stream);
+
 /* Static English name of a status code (never NULL). */
 const char* mha_status_string(mha_status status);
 

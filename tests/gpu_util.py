@@ -15,6 +15,12 @@ ROWSUM_TOL = 1e-3
 # and with it the exported log-sum-exp, can differ from the exact one by at
 # most log(1 + 2^-8), plus fp32 noise.
 LSE_TOL = {"bf16": math.log1p(2.0 ** -8) + 1e-5, "f32": 1e-5}
+# Encoder layer (LayerNorm outputs, magnitudes up to ~5): |got - ref| <= atol + rtol * |ref|.
+# bf16: the attention bar (2e-2) for the mixing arithmetic, plus 2^-7 relative:
+# the output's own rounding (half an ulp, 2^-9 relative) and the rounding of the
+# stored h carried through the second residual (another 2^-9 relative after
+# the norm), with a factor 2 of margin. fp32: the attention bar.
+ENC_TOL = {"bf16": (2e-2, 2.0 ** -7), "f32": (1e-4, 0.0)}
 
 
 def say(msg: str) -> None:

@@ -35,8 +35,8 @@ def lib():
 def test_header_declares_the_boundary():
     fns = header_functions()
     assert {"attention_forward", "attention_forward_padded", "mha_forward", "mha_forward_padded",
-            "mha_forward_workspace_size", "linear_forward", "mha_status_string", "mha_last_error",
-            "mha_version"} == set(fns)
+            "mha_forward_workspace_size", "linear_forward", "encoder_layer_workspace_size",
+            "encoder_layer_forward", "mha_status_string", "mha_last_error", "mha_version"} == set(fns)
     assert set(fns) == set(_lib.SIGNATURES), "binding signatures out of sync with include/mha.h"
 
 
@@ -203,3 +203,38 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         m.attention_forward(x, x, x)
+
+
+def enc(lib, weights=None, ws=FAKE, ws_bytes=1 << 40, B=2, n=16, dm=512, h=8, ff=2048, eps=1e-5,
+        dtype=_lib.MHA_BF16, causal=0, kv_len=None, x=FAKE):
+    if weights is None:
+        weights = _lib.EncoderWeights(*([FAKE] * 16))
+    return lib.encoder_layer_forward(x, ctypes.byref(weights) if weights is not False else None, FAKE, ws,
+                                     ws_bytes, B, n, dm, h, ff, eps, dtype, causal, kv_len, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(weights=False), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(weights=_lib.EncoderWeights(*([FAKE] * 15 + [None]))), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(weights=_lib.EncoderWeights(*([FAKE] * 10 + [MIS] + [FAKE] * 5))), _lib.MHA_ERR_INVALID_ARG, "aligned"),
+    (dict(eps=float("nan")), _lib.MHA_ERR_INVALID_ARG, "eps"),
+    (dict(eps=-1.0), _lib.MHA_ERR_INVALID_ARG, "eps"),
+    (dict(ff=2044), _lib.MHA_ERR_INVALID_ARG, "multiples of 8"),
+    (dict(dm=8192, h=128), _lib.MHA_ERR_UNSUPPORTED, "LayerNorm"),
+    (dict(ws=None), _lib.MHA_ERR_INVALID_ARG, "workspace"),
+    (dict(ws_bytes=1000), _lib.MHA_ERR_WORKSPACE, "too small"),
+    (dict(dm=256, h=8), _lib.MHA_ERR_UNSUPPORTED, "d_k = 64"),
+    (dict(kv_len=FAKE + 2), _lib.MHA_ERR_INVALID_ARG, "kv_len"),
+])
+def test_encoder_layer_validation(lib, kw, status, needle):
+    assert enc(lib, **kw) == status
+    assert needle in lib.mha_last_error().decode()
+
+
+def test_encoder_layer_workspace_size(lib):
+    def r(x):
+        return (x + 255) // 256 * 256
+    B, n, dm, ff = 32, 512, 512, 2048
+    assert lib.encoder_layer_workspace_size(B, n, dm, 8, ff, 1) == 4 * r(B * n * dm * 2) + r(B * n * ff * 2)
+    assert lib.encoder_layer_workspace_size(B, n, dm, 8, 0, 1) == 0

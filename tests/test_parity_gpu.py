@@ -14,7 +14,8 @@ import pytest
 import oracle
 import transformer_scaled_dot_mha_amd as mha
 import workloads
-from tests.gpu_util import LSE_TOL, ROWSUM_TOL, TOL, assert_close, device, max_abs, say, to_device, to_f64
+from tests.gpu_util import (ENC_TOL, LSE_TOL, ROWSUM_TOL, TOL, assert_close, device, max_abs, say, to_device,
+                             to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -362,3 +363,38 @@ def test_padded_mha_parity(dev, dtype):
     torch.cuda.synchronize()
     want = oracle.mha_ref(xs.value, xs.value, xs.value, *[s.value for s in ws], h, causal=True, kv_len=lens)
     assert_close(to_f64(out), want, dtype, "padded mha causal")
+
+
+# ---------------------------------------------------------------- encoder sub-layer (NEXT-2)
+def _oracle_params(ps):
+    m = {"ln1_gamma": "ln1_g", "ln1_beta": "ln1_b", "ln2_gamma": "ln2_g", "ln2_beta": "ln2_b"}
+    return {m.get(k, k): v.value for k, v in ps.items()}
+
+
+ENCODER_CASES = [
+    # (B, N, d_model, heads, d_ff, dtype, causal, lens)
+    (2, 100, 512, 8, 2048, "bf16", False, None),
+    (2, 300, 512, 8, 2048, "bf16", True, None),
+    (3, 130, 512, 8, 2048, "bf16", False, [130, 45, 0]),
+    (2, 70, 256, 4, 512, "f32", False, [70, 21]),
+    (1, 65, 128, 2, 256, "f32", True, None),
+]
+
+
+@pytest.mark.parametrize("B,N,dm,h,ff,dtype,causal,lens", ENCODER_CASES)
+def test_encoder_layer_parity(dev, B, N, dm, h, ff, dtype, causal, lens):
+    import torch
+    x = workloads.random_tensor((B, N, dm), dtype, seed=1100 + N)
+    ps = workloads.encoder_params(dm, ff, dtype, seed=1200 + dm)
+    kv_len = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=dev)
+    say(f"encoder layer {B}x{N} d={dm} h={h} ff={ff} {dtype} causal={causal} lens={lens}")
+    out = mha.encoder_layer_forward(to_device(x, dev), {k: to_device(v, dev) for k, v in ps.items()}, h,
+                                    causal=causal, kv_len=kv_len)
+    torch.cuda.synchronize()
+    want = oracle.encoder_layer_ref(x.value, _oracle_params(ps), h, causal=causal, kv_len=lens)
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - want)
+    bound = ENC_TOL[dtype][0] + ENC_TOL[dtype][1] * np.abs(want)
+    say(f"encoder layer max-abs {err.max():.3e}, worst ratio to bound {float((err / bound).max()):.3f}")
+    assert np.all(err <= bound), f"max-abs {err.max():.3e}"

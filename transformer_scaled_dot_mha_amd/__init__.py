@@ -8,12 +8,15 @@ PyTorch fallback, and calling with CPU tensors raises.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 
-from ._lib import (MHA_BF16, MHA_ERR_HIP, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED,
+from ._lib import (ENCODER_WEIGHT_NAMES, EncoderWeights, MHA_BF16, MHA_ERR_HIP, MHA_ERR_INVALID_ARG,
+                   MHA_ERR_UNSUPPORTED,
                    MHA_ERR_WORKSPACE, MHA_F32, MHA_OK, LIB_PATH, MHAError, check, load, strides3)
 
-__all__ = ["attention_forward", "linear_forward", "mha_forward", "mha_forward_workspace_size",
+__all__ = ["attention_forward", "encoder_layer_forward", "encoder_layer_workspace_size", "linear_forward",
+           "mha_forward", "mha_forward_workspace_size",
            "MHAError", "MHA_F32", "MHA_BF16", "LIB_PATH", "load"]
 
 
@@ -174,5 +177,55 @@ def mha_forward(xq, xk, xv, wq, wk, wv, wo, heads: int, *, causal: bool = False,
             st = lib.mha_forward(*args, _stream_handle(dev, stream))
         else:
             st = lib.mha_forward_padded(*args, _kv_len_arg(kv_len, B, dev), _stream_handle(dev, stream))
+    check(st)
+    return out
+
+
+def encoder_layer_workspace_size(batch: int, n: int, d_model: int, heads: int, d_ff: int, dtype) -> int:
+    """Bytes of workspace encoder_layer_forward needs (dtype: torch dtype or MHA_F32/MHA_BF16)."""
+    code = dtype if isinstance(dtype, int) else (MHA_BF16 if str(dtype).endswith("bfloat16") else MHA_F32)
+    return int(load().encoder_layer_workspace_size(batch, n, d_model, heads, d_ff, code))
+
+
+def encoder_layer_forward(x, weights: dict, heads: int, *, eps: float = 1e-5, causal: bool = False, kv_len=None,
+                          out=None, workspace=None, stream=None):
+    """One post-norm encoder layer: LayerNorm(h + FFN(h)) with h = LayerNorm(x + MHA(x)).
+
+    x (B, N, d_model). weights: dict of device tensors named wq, wk, wv, wo,
+    bq, bk, bv, bo, ln1_gamma, ln1_beta, w1, b1, w2, b2, ln2_gamma, ln2_beta,
+    matrices stored (in, out): w1 (d_model, d_ff), w2 (d_ff, d_model).
+    kv_len: optional int32 device tensor (B,) of key lengths (padding mask).
+    """
+    torch = _torch()
+    missing = [n for n in ENCODER_WEIGHT_NAMES if n not in weights]
+    if missing:
+        raise KeyError(f"missing encoder weights: {missing}")
+    ts = [weights[n] for n in ENCODER_WEIGHT_NAMES]
+    dev = _require_device(x, *ts)
+    B, N, d_model = x.shape
+    d_ff = weights["w1"].shape[1]
+    shapes = {"wq": (d_model, d_model), "wk": (d_model, d_model), "wv": (d_model, d_model),
+              "wo": (d_model, d_model), "w1": (d_model, d_ff), "w2": (d_ff, d_model), "b1": (d_ff,)}
+    for n in ENCODER_WEIGHT_NAMES:
+        want = shapes.get(n, (d_model,))
+        if tuple(weights[n].shape) != want or not weights[n].is_contiguous():
+            raise ValueError(f"{n} must be a contiguous {want} tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    code = _dtype_code(x)
+    lib = load()
+    need = int(lib.encoder_layer_workspace_size(B, N, d_model, heads, d_ff, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(x)
+    if tuple(out.shape) != (B, N, d_model) or not out.is_contiguous() or out.dtype != x.dtype:
+        raise ValueError("out must be a contiguous (B, N, d_model) tensor of x's dtype")
+    w = EncoderWeights(*[t.data_ptr() for t in ts])
+    kvp = None if kv_len is None else _kv_len_arg(kv_len, B, dev)
+    with torch.cuda.device(dev):
+        st = lib.encoder_layer_forward(x.data_ptr(), ctypes.byref(w), out.data_ptr(), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), B, N, d_model, heads, d_ff,
+                                       float(eps), code, int(bool(causal)), kvp, _stream_handle(dev, stream))
     check(st)
     return out

@@ -18,6 +18,15 @@ _i64x3 = ctypes.POINTER(ctypes.c_int64)
 _vp = ctypes.c_void_p
 _int = ctypes.c_int
 
+ENCODER_WEIGHT_NAMES = ("wq", "wk", "wv", "wo", "bq", "bk", "bv", "bo", "ln1_gamma", "ln1_beta",
+                        "w1", "b1", "w2", "b2", "ln2_gamma", "ln2_beta")
+
+
+class EncoderWeights(ctypes.Structure):
+    """mha_encoder_weights of include/mha.h: sixteen device pointers."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ENCODER_WEIGHT_NAMES]
+
+
 # name -> (restype, argtypes); must match include/mha.h
 SIGNATURES = {
     "attention_forward": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int,
@@ -33,6 +42,9 @@ SIGNATURES = {
                            _int, _int, _int, _int, _int, _int, _int, _vp]),
     "mha_forward_padded": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   _int, _int, _int, _int, _int, _int, _int, _vp, _vp]),
+    "encoder_layer_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int, _int, _int]),
+    "encoder_layer_forward": (_int, [_vp, ctypes.POINTER(EncoderWeights), _vp, _vp, ctypes.c_size_t, _int, _int,
+                                     _int, _int, _int, ctypes.c_float, _int, _int, _vp, _vp]),
     "mha_status_string": (ctypes.c_char_p, [_int]),
     "mha_last_error": (ctypes.c_char_p, []),
     "mha_version": (_int, []),

@@ -34,16 +34,32 @@ struct LinearGroup {
   void* y;
   int m;
   int64_t ldx, ldw, ldy;
+  const void* bias;  // nullable, (n) of the element type: added to every row
 };
 struct LinearArgs {
   LinearGroup g[3];
   int groups;
   int n, k;
+  int relu;  // 1: max(0, .) after the bias
+};
+
+// out[r, :] = LayerNorm(x[r, :] + y[r, :]) * gamma + beta over d columns, rows
+// contiguous (leading dimension d); statistics in fp32.
+struct AddNormArgs {
+  const void* x;
+  const void* y;
+  const void* gamma;
+  const void* beta;
+  void* out;
+  int rows, d;
+  float eps;
 };
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream);
+hipError_t launch_add_layernorm_bf16(const AddNormArgs& a, hipStream_t stream);
+hipError_t launch_add_layernorm_f32(const AddNormArgs& a, hipStream_t stream);
 
 }  // namespace mha

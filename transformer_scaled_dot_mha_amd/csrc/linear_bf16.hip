@@ -163,12 +163,31 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
 
   // lane holds row 64*wave + 32*mb + lq and columns 32*nb + 8*q + 4*hf + 0..3;
   // the two halves swap groups so that each lane writes 16-byte row chunks.
+  // Optional epilogue: + bias[column], then max(0, .), in fp32 before rounding.
+  const bf16* Bias = static_cast<const bf16*>(g.bias);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int row = 64 * wave + 32 * mb + lq;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const f32x16& v = acc[nb][mb];
+      f32x16 v = acc[nb][mb];
+      if (Bias != nullptr) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // columns 32*nb + 8*q + 4*hf + 0..3 lie in one 8-column chunk: all valid or none
+          if (32 * nb + 8 * q < valid_n) {
+            const u32x2 bw = *reinterpret_cast<const u32x2*>(Bias + n0 + 32 * nb + 8 * q + 4 * hf);
+            v[4 * q] += __builtin_bit_cast(float, bw[0] << 16);
+            v[4 * q + 1] += __builtin_bit_cast(float, bw[0] & 0xffff0000u);
+            v[4 * q + 2] += __builtin_bit_cast(float, bw[1] << 16);
+            v[4 * q + 3] += __builtin_bit_cast(float, bw[1] & 0xffff0000u);
+          }
+        }
+      }
+      if (args.relu) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = __builtin_fmaxf(v[r], 0.f);
+      }
       unsigned w[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

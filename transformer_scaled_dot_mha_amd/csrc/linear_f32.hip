@@ -4,7 +4,8 @@
 // fp32 workloads: X (m, k) row-major, W (k, n) row-major (in, out), Y (m, n)
 // row-major ("The Transformer" (hoshank.vercel.app), "The Mathematics",
 // MultiHead equation). 64 x 64 output tile per workgroup of 256 threads, each
-// thread 4 x 4 outputs, 16-deep k steps staged through LDS.
+// thread 4 x 4 outputs, 16-deep k steps staged through LDS. Optional epilogue:
+// a bias per column and a ReLU (the FFN's max(0, x W1 + b1)).
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -60,7 +61,12 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(LinearArgs args, int ti
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + 4 * tx + j;
-      if (col < n) Y[(int64_t)row * g.ldy + col] = acc[i][j];
+      if (col < n) {
+        // optional epilogue: + bias[column], then max(0, .)
+        float v = acc[i][j] + (g.bias != nullptr ? static_cast<const float*>(g.bias)[col] : 0.f);
+        if (args.relu) v = fmaxf(v, 0.f);
+        Y[(int64_t)row * g.ldy + col] = v;
+      }
     }
   }
 }

@@ -176,9 +176,16 @@ mha_status attention_impl(const void* q, const void* k, const void* v, void* o, 
   return run_attention(a, dtype, static_cast<hipStream_t>(stream));
 }
 
+// Projection biases of the attention module (all null for the bias-free
+// MultiHead of the pages' equation).
+struct MhaBiases {
+  const void *q = nullptr, *k = nullptr, *v = nullptr, *o = nullptr;
+};
+
 mha_status mha_impl(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk, const void* wv,
                     const void* wo, void* out, void* workspace, size_t workspace_bytes, int batch, int n_q, int n_k,
-                    int d_model, int heads, mha_dtype dtype, int causal, const int32_t* kv_len, void* stream) {
+                    int d_model, int heads, mha_dtype dtype, int causal, const int32_t* kv_len, void* stream,
+                    const MhaBiases& bias = MhaBiases()) {
   if (!xq || !xk || !xv || !wq || !wk || !wv || !wo || !out)
     return fail(MHA_ERR_INVALID_ARG, "inputs, weights and out must be non-null");
   if (!workspace) return fail(MHA_ERR_INVALID_ARG, "workspace must be non-null");
@@ -218,9 +225,9 @@ mha_status mha_impl(const void* xq, const void* xk, const void* xv, const void* 
   // (1) Q, K, V projections in one grouped launch; row-major (rows, d_model)
   //     is already the head-split (batch, n, heads, d) layout.
   mha::LinearArgs lin = {};
-  lin.g[0] = mha::LinearGroup{xq, wq, qw, (int)rows_q, d_model, d_model, d_model};
-  lin.g[1] = mha::LinearGroup{xk, wk, kw, (int)rows_k, d_model, d_model, d_model};
-  lin.g[2] = mha::LinearGroup{xv, wv, vw, (int)rows_k, d_model, d_model, d_model};
+  lin.g[0] = mha::LinearGroup{xq, wq, qw, (int)rows_q, d_model, d_model, d_model, bias.q};
+  lin.g[1] = mha::LinearGroup{xk, wk, kw, (int)rows_k, d_model, d_model, d_model, bias.k};
+  lin.g[2] = mha::LinearGroup{xv, wv, vw, (int)rows_k, d_model, d_model, d_model, bias.v};
   lin.groups = 3;
   lin.n = d_model;
   lin.k = d_model;
@@ -238,11 +245,94 @@ mha_status mha_impl(const void* xq, const void* xk, const void* xv, const void* 
 
   // (3) output projection W^O
   mha::LinearArgs out_lin = {};
-  out_lin.g[0] = mha::LinearGroup{ow, wo, out, (int)rows_q, d_model, d_model, d_model};
+  out_lin.g[0] = mha::LinearGroup{ow, wo, out, (int)rows_q, d_model, d_model, d_model, bias.o};
   out_lin.groups = 1;
   out_lin.n = d_model;
   out_lin.k = d_model;
   return run_linear(out_lin, dtype, st);
+}
+
+constexpr int kMaxNormWidth = 4096;  // the residual + LayerNorm kernel holds a row in one wavefront
+
+bool enc_ws_layout(int batch, int n, int d_model, int d_ff, mha_dtype t, WsLayout* w, size_t* ffh, size_t* total) {
+  if (!ws_layout(batch, n, n, d_model, t, w)) return false;
+  const unsigned __int128 rf = (unsigned __int128)batch * n * d_ff * elem_bytes(t);
+  if (rf > ((unsigned __int128)1 << 60)) return false;
+  *ffh = w->total;
+  *total = w->total + round_up((size_t)rf);
+  return true;
+}
+
+mha_status run_add_norm(const mha::AddNormArgs& a, mha_dtype dtype, hipStream_t stream) {
+  hipError_t e = dtype == MHA_BF16 ? mha::launch_add_layernorm_bf16(a, stream) : mha::launch_add_layernorm_f32(a, stream);
+  return hip_status(e, "layer norm launch");
+}
+
+mha_status encoder_layer_impl(const void* x, const mha_encoder_weights* wts, void* out, void* workspace,
+                              size_t workspace_bytes, int batch, int n, int d_model, int heads, int d_ff, float eps,
+                              mha_dtype dtype, int causal, const int32_t* kv_len, void* stream) {
+  if (!x || !out || !wts) return fail(MHA_ERR_INVALID_ARG, "x, weights and out must be non-null");
+  const void* ptrs[16] = {wts->wq, wts->wk, wts->wv, wts->wo, wts->bq, wts->bk, wts->bv, wts->bo,
+                          wts->ln1_gamma, wts->ln1_beta, wts->w1, wts->b1, wts->w2, wts->b2, wts->ln2_gamma,
+                          wts->ln2_beta};
+  for (const void* p : ptrs) {
+    if (!p) return fail(MHA_ERR_INVALID_ARG, "every weight, bias and norm parameter must be non-null");
+    if (!aligned16(p)) return fail(MHA_ERR_INVALID_ARG, "every weight, bias and norm parameter must be 16-byte aligned");
+  }
+  if (!valid_dtype((int)dtype)) return fail(MHA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (batch < 1 || n < 1 || d_model < 1 || heads < 1 || d_ff < 1)
+    return fail(MHA_ERR_INVALID_ARG, "sizes must be >= 1 (batch=%d n=%d d_model=%d heads=%d d_ff=%d)", batch, n,
+                d_model, heads, d_ff);
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(MHA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const int vec = vec_elems(dtype);
+  if (d_model % vec || d_ff % vec)
+    return fail(MHA_ERR_INVALID_ARG, "d_model and d_ff must be multiples of %d", vec);
+  if (d_model > kMaxNormWidth)
+    return fail(MHA_ERR_UNSUPPORTED, "d_model (%d) above %d: one row must fit the LayerNorm wavefront", d_model,
+                kMaxNormWidth);
+  if (d_ff > kMaxLdX) return fail(MHA_ERR_UNSUPPORTED, "d_ff (%d) too large, at most %lld", d_ff, (long long)kMaxLdX);
+  WsLayout w;
+  size_t ffh_off = 0, total = 0;
+  if (!enc_ws_layout(batch, n, d_model, d_ff, dtype, &w, &ffh_off, &total))
+    return fail(MHA_ERR_UNSUPPORTED, "workspace size overflows");
+  if (workspace && workspace_bytes < total)
+    return fail(MHA_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, total);
+  if ((int64_t)batch * n > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "batch * sequence too large");
+  const int rows = batch * n;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // (1) attention sub-layer with biases; its output t1 lands in the Q region
+  //     (Q is dead once the attention launch has read it)
+  void* t1 = ws ? ws + w.q : nullptr;
+  MhaBiases b;
+  b.q = wts->bq, b.k = wts->bk, b.v = wts->bv, b.o = wts->bo;
+  mha_status s = mha_impl(x, x, x, wts->wq, wts->wk, wts->wv, wts->wo, t1, workspace, workspace_bytes, batch, n, n,
+                          d_model, heads, dtype, causal, kv_len, stream, b);
+  if (s != MHA_OK) return s;
+  // the attention launch reads Q before W^O writes t1 into its region: same stream, in order
+
+  // (2) h = LayerNorm(x + t1), into the K region
+  void* h = ws + w.k;
+  s = run_add_norm(mha::AddNormArgs{x, t1, wts->ln1_gamma, wts->ln1_beta, h, rows, d_model, eps}, dtype, st);
+  if (s != MHA_OK) return s;
+
+  // (3) FFN: hidden = max(0, h W1 + b1), then t2 = hidden W2 + b2 into the V region
+  void* hid = ws + ffh_off;
+  mha::LinearArgs l1 = {};
+  l1.g[0] = mha::LinearGroup{h, wts->w1, hid, rows, d_model, d_ff, d_ff, wts->b1};
+  l1.groups = 1, l1.n = d_ff, l1.k = d_model, l1.relu = 1;
+  s = run_linear(l1, dtype, st);
+  if (s != MHA_OK) return s;
+  void* t2 = ws + w.v;
+  mha::LinearArgs l2 = {};
+  l2.g[0] = mha::LinearGroup{hid, wts->w2, t2, rows, d_ff, d_model, d_model, wts->b2};
+  l2.groups = 1, l2.n = d_model, l2.k = d_ff;
+  s = run_linear(l2, dtype, st);
+  if (s != MHA_OK) return s;
+
+  // (4) out = LayerNorm(h + t2)
+  return run_add_norm(mha::AddNormArgs{h, t2, wts->ln2_gamma, wts->ln2_beta, out, rows, d_model, eps}, dtype, st);
 }
 
 }  // namespace
@@ -338,6 +428,27 @@ mha_status mha_forward_padded(const void* xq, const void* xk, const void* xv, co
                     dtype, causal, kv_len, stream);
   } catch (...) {
     return fail(MHA_ERR_HIP, "internal error in mha_forward_padded");
+  }
+}
+
+size_t encoder_layer_workspace_size(int batch, int n, int d_model, int heads, int d_ff, mha_dtype dtype) {
+  if (batch < 1 || n < 1 || d_model < 1 || heads < 1 || d_ff < 1 || !valid_dtype((int)dtype)) return 0;
+  WsLayout w;
+  size_t ffh = 0, total = 0;
+  if (!enc_ws_layout(batch, n, d_model, d_ff, dtype, &w, &ffh, &total)) return 0;
+  return total;
+}
+
+mha_status encoder_layer_forward(const void* x, const mha_encoder_weights* weights, void* out, void* workspace,
+                                 size_t workspace_bytes, int batch, int n, int d_model, int heads, int d_ff, float eps,
+                                 mha_dtype dtype, int causal, const int32_t* kv_len, void* stream) {
+  try {
+    if (kv_len && !aligned4(kv_len)) return fail(MHA_ERR_INVALID_ARG, "kv_len must be 4-byte aligned");
+    if (!workspace) return fail(MHA_ERR_INVALID_ARG, "workspace must be non-null");
+    return encoder_layer_impl(x, weights, out, workspace, workspace_bytes, batch, n, d_model, heads, d_ff, eps, dtype,
+                              causal, kv_len, stream);
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in encoder_layer_forward");
   }
 }
 

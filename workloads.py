@@ -205,6 +205,31 @@ def make_inputs(w: Workload, *, v_ones: bool = False) -> dict[str, Stored]:
     return out
 
 
+ENCODER_PARAM_NAMES = ("wq", "wk", "wv", "wo", "bq", "bk", "bv", "bo", "ln1_gamma", "ln1_beta",
+                       "w1", "b1", "w2", "b2", "ln2_gamma", "ln2_beta")
+
+
+def encoder_params(d_model: int, d_ff: int, dtype: str, seed: int) -> dict[str, Stored]:
+    """Seeded encoder-layer parameters, drawn in ENCODER_PARAM_NAMES order from
+    ``default_rng(seed)``: matrices (in, out) N(0, 1/fan_in) so activations stay
+    unit variance; biases and LayerNorm shifts N(0, 0.1^2); LayerNorm scales
+    1 + N(0, 0.1^2)."""
+    rng = np.random.default_rng(seed)
+    shapes = {"w1": (d_model, d_ff), "b1": (d_ff,), "w2": (d_ff, d_model)}
+    out = {}
+    for name in ENCODER_PARAM_NAMES:
+        shape = shapes.get(name, (d_model, d_model) if name in ("wq", "wk", "wv", "wo") else (d_model,))
+        z = rng.standard_normal(shape)
+        if len(shape) == 2:
+            z = z / math.sqrt(shape[0])
+        elif name.endswith("gamma"):
+            z = 1.0 + 0.1 * z
+        else:
+            z = 0.1 * z
+        out[name] = store(z, dtype)
+    return out
+
+
 def random_tensor(shape, dtype: str, seed: int, scale: float = 1.0) -> Stored:
     """A seeded unit-normal tensor (times scale) for edge-shape tests."""
     rng = np.random.default_rng(seed)
