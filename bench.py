@@ -103,7 +103,13 @@ def cpu_baseline(w, inputs, min_seconds=10.0, max_seconds=30.0):
     import oracle
     info = threadpoolctl.threadpool_info()
     threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
-    if w.kind == "mha":
+    if w.kind == "layer":
+        names = {"ln1_gamma": "ln1_g", "ln1_beta": "ln1_b", "ln2_gamma": "ln2_g", "ln2_beta": "ln2_b"}
+        params = {names.get(k, k): v.value for k, v in inputs.items() if k != "x"}
+        fn = lambda: oracle.encoder_layer_ref(inputs["x"].value, params, w.heads)
+        flops = w.total_flops()
+        sample = f"the full workload ({w.batch} batch elements), oracle.encoder_layer_ref in float64"
+    elif w.kind == "mha":
         xv = inputs["x"].value
         args = (xv, xv, xv, inputs["wq"].value, inputs["wk"].value, inputs["wv"].value, inputs["wo"].value)
         fn = lambda: oracle.mha_ref(*args, w.heads, causal=w.causal, kv_len=w.kv_lengths())
@@ -139,7 +145,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="encoder", help="encoder | tiny | decoder | cross | long | padded")
+    ap.add_argument("--workload", default="encoder",
+                    help="encoder | tiny | decoder | cross | long | padded | layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the long causal attention line")
     ap.add_argument("--calib-copy", action="store_true",
@@ -166,7 +173,35 @@ def main():
     result = {}
     lens = w.kv_lengths()
     kv_len = None if lens is None else torch.from_numpy(lens).to(dev)
-    if w.kind == "mha":
+    if w.kind == "layer":
+        dm, ff = w.d_model, w.d_ff
+        x = torch_tensor(inputs["x"], dev)
+        params = {k: torch_tensor(v, dev) for k, v in inputs.items() if k != "x"}
+        per_set = x.numel() * x.element_size() * 2
+        n_sets = max(1, math.ceil(ROTATE_BYTES / per_set))
+        xs = [x] + [x.clone() for _ in range(n_sets - 1)]
+        outs = [torch.empty_like(x) for _ in range(n_sets)]
+        need = mha.encoder_layer_workspace_size(w.batch, w.n_q, dm, w.heads, ff, x.dtype)
+        work = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def step(i):
+            mha.encoder_layer_forward(xs[i % n_sets], params, w.heads, kv_len=kv_len, out=outs[i % n_sets],
+                                      workspace=work)
+
+        step(0)
+        torch.cuda.synchronize()
+        flops_step = w.total_flops()
+        # dominant kernel: the FFN's first product (rows x d_model by d_model x d_ff, the largest
+        # launch of the layer), re-timed alone on workspace-sized buffers; same kernel, same grid
+        rows = w.batch * w.n_q
+        h_in = torch.empty((rows, dm), dtype=x.dtype, device=dev).copy_(x.view(rows, dm))
+        hid = torch.empty((rows, ff), dtype=x.dtype, device=dev)
+        dom_fn = lambda i: mha.linear_forward(h_in, params["w1"], out=hid)
+        dom_flops = 2 * rows * dm * ff
+        dom_name = "linear_bf16_kernel"
+        dom_bytes = (rows * dm + dm * ff + rows * ff) * x.element_size()
+        get_out = lambda: outs[0]
+    elif w.kind == "mha":
         dm = w.d_model
         x = torch_tensor(inputs["x"], dev)
         ws = [torch_tensor(inputs[n], dev) for n in ("wq", "wk", "wv", "wo")]
@@ -239,7 +274,7 @@ def main():
     launch_desc = f"{dom_name}:{w.name}"
     roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic_for("attention", launch_desc),
+                "traffic": traffic_for("linear" if dom_name.startswith("linear") else "attention", launch_desc),
                 "algorithmic_bytes": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
                 "achieved_gbps": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1)}
     log(f"dominant kernel {dom_name}: {dom_ms * 1e3:.1f} us, {achieved:.1f} TFLOP/s")
@@ -274,16 +309,20 @@ def main():
         got = get_out().float().cpu().numpy().astype(np.float64)
         if w.kind == "attn" and w.oracle_rows:
             got = got[:, :, workloads.sample_rows(w)]
-        ref_o = ref if w.kind == "mha" else ref[0]
+        ref_o = ref if w.kind in ("mha", "layer") else ref[0]
         err = float(np.max(np.abs(got - ref_o)))
         result["parity_max_abs"] = err
         log(f"parity vs oracle: max-abs {err:.3e}")
 
     cfg = {"workload": w.name, "batch": w.batch, "seq_len_q": w.n_q, "seq_len_k": w.n_k, "heads": w.heads,
            "d_k": w.d_k, "causal": w.causal,
-           "step": "mha_forward: QKV projections + attention + W^O" if w.kind == "mha" else "attention_forward"}
-    if w.kind == "mha":
+           "step": {"mha": "mha_forward: QKV projections + attention + W^O",
+                    "layer": "encoder_layer_forward: attention sub-layer + residual LayerNorm + FFN + residual "
+                             "LayerNorm"}.get(w.kind, "attention_forward")}
+    if w.kind in ("mha", "layer"):
         cfg["d_model"] = w.d_model
+    if w.kind == "layer":
+        cfg["d_ff"] = w.d_ff
     if lens is not None:
         cfg["kv_len"] = (f"per-batch key lengths uniform in [{w.kv_len_range[0]}, {w.kv_len_range[1]}] "
                          f"(seeded; mean {float(lens.mean()):.1f})")

@@ -29,7 +29,8 @@ import numpy as np
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mha": projections + attention + W^O;  "attn": attention core only
+    kind: str            # "mha": projections + attention + W^O;  "attn": attention core only;
+                         # "layer": a whole encoder layer (attention sub-layer, FFN, two residual norms)
     dtype: str           # "f32" or "bf16": the stored type of every tensor
     batch: int
     heads: int
@@ -41,6 +42,7 @@ class Workload:
     d_model: int = 0     # mha workloads only
     oracle_rows: int = 0  # >0: the oracle checks this many sampled query positions
     kv_len_range: tuple = ()  # (lo, hi): per-batch key lengths drawn uniformly in [lo, hi] (padding mask)
+    d_ff: int = 0        # layer workloads only: FFN inner width
 
     def kv_lengths(self):
         """Per-batch key lengths of a padded workload (None if unpadded), from
@@ -81,7 +83,7 @@ class Workload:
         return 4 * self.heads * self.d_k * self.total_pairs()
 
     def projection_flops(self) -> int:
-        if self.kind != "mha":
+        if self.kind not in ("mha", "layer"):
             return 0
         dm = self.d_model
         rows_q = self.batch * self.n_q
@@ -89,8 +91,14 @@ class Workload:
         # Q, K, V projections and the output projection W^O
         return 2 * dm * dm * (rows_q + 2 * rows_k + rows_q)
 
+    def ffn_flops(self) -> int:
+        """The FFN's two products, 2 * rows * d_model * d_ff each (biases, ReLU and norms not counted)."""
+        if self.kind != "layer":
+            return 0
+        return 2 * 2 * self.batch * self.n_q * self.d_model * self.d_ff
+
     def total_flops(self) -> int:
-        return self.attention_flops() + self.projection_flops()
+        return self.attention_flops() + self.projection_flops() + self.ffn_flops()
 
 
 WORKLOADS: dict[str, Workload] = {
@@ -109,6 +117,9 @@ WORKLOADS: dict[str, Workload] = {
         # the base encoder over a padded batch: key lengths uniform in [64, 512]
         Workload("base_encoder_padded_mha_bf16_b32_n512", "mha", "bf16", batch=32, heads=8,
                  n_q=512, n_k=512, d_k=64, causal=False, seed=6, d_model=512, kv_len_range=(64, 512)),
+        # one whole encoder layer of the base model (d_ff = 2048)
+        Workload("base_encoder_layer_bf16_b32_n512", "layer", "bf16", batch=32, heads=8,
+                 n_q=512, n_k=512, d_k=64, causal=False, seed=7, d_model=512, d_ff=2048),
     ]
 }
 
@@ -120,6 +131,7 @@ ALIASES = {
     "cross": "cross_attn_bf16_b32_h8_nq384_nk512",
     "long": "long_causal_bf16_b2_h16_n8192",
     "padded": "base_encoder_padded_mha_bf16_b32_n512",
+    "layer": "base_encoder_layer_bf16_b32_n512",
 }
 
 
@@ -183,12 +195,17 @@ def make_inputs(w: Workload, *, v_ones: bool = False) -> dict[str, Stored]:
     mha:  x (B, N, d_model), then W^Q, W^K, W^V, W^O, each (d_model, d_model),
           stored (in, out) so that Q = x @ W^Q. Self-attention: one x serves
           as the query, key and value input.
+    layer: x (B, N, d_model), then encoder_params(d_model, d_ff, seed=100 + seed).
     attn: Q (B, H, N_q, d), K (B, H, N_k, d), V (B, H, N_k, d).
     v_ones replaces V by all ones after drawing (row-sum checks); the draws
     themselves are unchanged so Q and K stay identical to the plain run.
     """
     rng = np.random.default_rng(w.seed)
     out: dict[str, Stored] = {}
+    if w.kind == "layer":
+        out["x"] = store(rng.standard_normal((w.batch, w.n_q, w.d_model)), w.dtype)
+        out.update(encoder_params(w.d_model, w.d_ff, w.dtype, seed=100 + w.seed))
+        return out
     if w.kind == "mha":
         dm = w.d_model
         out["x"] = store(rng.standard_normal((w.batch, w.n_q, dm)), w.dtype)
