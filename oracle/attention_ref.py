@@ -259,6 +259,29 @@ def encoder_layer_ref(x: np.ndarray, p: dict, heads: int, *, eps: float = 1e-5, 
     return layer_norm_ref(h + f, p["ln2_g"], p["ln2_b"], eps)
 
 
+def gather_pages(pool: np.ndarray, block_table, page_size: int, length: int) -> np.ndarray:
+    """Keys (or values) 0..length-1 of one sequence stored in fixed-size pages:
+    logical position j sits in page block_table[j // page_size] at row
+    j % page_size. pool: (num_pages, page_size, H, d) -> (H, length, d)."""
+    pool = np.asarray(pool, dtype=np.float64)
+    rows = [pool[int(block_table[j // page_size]), j % page_size] for j in range(length)]
+    if not rows:
+        return np.zeros((pool.shape[2], 0, pool.shape[3]))
+    return np.stack(rows, axis=1)
+
+
+def decode_ref(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, kv_len, *, scale: float | None = None):
+    """One decoding step: each (batch, head) query attends to the first
+    kv_len[b] cached keys and values -- the newest row of causal attention,
+    where position i sees keys j <= i ("How Transformers Work", the decoder
+    generating left to right; "The Transformer" (rayaq.ca), "Masks: who may
+    look at whom"). q: (B, H, d); k_cache, v_cache: (B, H, N_max, d).
+    Returns (O (B, H, d), lse (B, H)); a length of 0 gives O = 0, lse = -inf."""
+    q = np.asarray(q, dtype=np.float64)
+    o, _, lse = attention_ref(q[:, :, None, :], k_cache, v_cache, scale=scale, kv_len=kv_len)
+    return o[:, :, 0, :], lse[:, :, 0]
+
+
 def linear_ref(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     """One projection Y = X W (no bias), the per-head projection of the
     MultiHead equation ("The Transformer" (hoshank.vercel.app), "The

@@ -581,6 +581,37 @@ def check_encoder_layer_params():
     assert sum(v.size for v in p.values()) == sizes["encoder_layer_params"]
 
 
+# ------------------------------------------------------------------ decoding against a K/V cache
+def check_decode_is_last_causal_row(decode, attn):
+    """Generating left to right, the newest token's query sees every cached key
+    up to and including its own position: one decoding step equals the last row
+    of causal attention over the sequence so far ("How Transformers Work";
+    "The Transformer" (rayaq.ca), "Masks: who may look at whom")."""
+    q, k, v = _qkv(60, B=3, H=2, nq=9, nk=9, d=4)
+    full, _, full_lse = attn(q, k, v, causal=True)
+    for L in (1, 5, 9):
+        o, lse = decode(q[:, :, L - 1], k, v, [L] * 3)
+        assert np.allclose(o, full[:, :, L - 1], rtol=0, atol=1e-14), f"decode at length {L}"
+        assert np.allclose(lse, full_lse[:, :, L - 1], rtol=0, atol=1e-14)
+    o, lse = decode(q[:, :, 0], k, v, [0, 3, 9])
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(lse[0])), "an empty cache gives 0 and lse -inf"
+
+
+def check_paged_gather(gather):
+    """A sequence stored in pages, in any page order, reads back as the
+    contiguous sequence (the cache layout only moves rows, it computes nothing)."""
+    r = _rng(61)
+    H, d, P = 2, 3, 4
+    seq = r.standard_normal((H, 10, d))
+    order = [5, 0, 3]                                # logical page i lives in physical page order[i]
+    pool = np.zeros((6, P, H, d))
+    for i, pg in enumerate(order):
+        chunk = seq[:, i * P:(i + 1) * P]
+        pool[pg, :chunk.shape[1]] = chunk.transpose(1, 0, 2)
+    assert np.array_equal(gather(pool, order, P, 10), seq)
+    assert gather(pool, order, P, 0).shape == (H, 0, d)
+
+
 ATTENTION_PINS = [check_rows_sum_to_one, check_permutation_equivariance,
                   check_constant_v_and_convex_hull, check_causal_locality,
                   check_masked_weight_is_zero, check_closed_forms, check_low_temperature_argmax,

@@ -104,3 +104,11 @@ def test_encoder_layer_structure():
 
 def test_encoder_layer_params():
     pins.check_encoder_layer_params()
+
+
+def test_decode_is_last_causal_row():
+    pins.check_decode_is_last_causal_row(oracle.decode_ref, oracle.attention_ref)
+
+
+def test_paged_gather():
+    pins.check_paged_gather(oracle.gather_pages)

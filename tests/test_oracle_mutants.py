@@ -209,3 +209,51 @@ def test_unmutated_layer_passes():
     pins.check_ffn(ffn)
     pins.check_encoder_layer_torch(layer)
     pins.check_encoder_layer_structure(layer, ln, ffn, oracle.mha_ref)
+
+
+def _mutant_decode(mutation):
+    """One decoding step or the page gather with one planted mistake."""
+    def decode(q, k, v, kv_len, *, scale=None):
+        L = np.asarray(kv_len)
+        if mutation == "decode_length_minus_one":
+            L = np.maximum(L - 1, 0)
+        elif mutation == "decode_length_plus_one":
+            L = np.minimum(L + 1, np.asarray(k).shape[2])
+        qq = np.asarray(q, np.float64)
+        if mutation == "decode_scale_missing":
+            qq = qq * math.sqrt(qq.shape[-1])
+        return oracle.decode_ref(qq, k, v, L, scale=scale)
+
+    def gather(pool, table, P, length):
+        pool = np.asarray(pool, np.float64)
+        if mutation == "pages_in_logical_order":
+            table = list(range(len(table)))
+        rows = []
+        for j in range(length):
+            pg, r = int(table[j // P]), j % P
+            if mutation == "page_row_reversed":
+                r = P - 1 - r
+            rows.append(pool[pg, r])
+        if not rows:
+            return np.zeros((pool.shape[2], 0, pool.shape[3]))
+        out = np.stack(rows, axis=1)
+        return out[::-1] if mutation == "heads_swapped" else out
+    return decode, gather
+
+
+DECODE_MUTANTS = ["decode_length_minus_one", "decode_length_plus_one", "decode_scale_missing",
+                  "pages_in_logical_order", "page_row_reversed", "heads_swapped"]
+
+
+@pytest.mark.parametrize("mutation", DECODE_MUTANTS)
+def test_decode_mutant_is_caught(mutation):
+    decode, gather = _mutant_decode(mutation)
+    checks = [lambda: pins.check_decode_is_last_causal_row(decode, oracle.attention_ref),
+              lambda: pins.check_paged_gather(gather)]
+    assert any(_caught(c) for c in checks), f"no pin catches the mutant {mutation!r}"
+
+
+def test_unmutated_decode_passes():
+    decode, gather = _mutant_decode("none")
+    pins.check_decode_is_last_causal_row(decode, oracle.attention_ref)
+    pins.check_paged_gather(gather)
