@@ -7,7 +7,9 @@ A step is one pass of the whole hot path over one batch of synthetic input.
 Default workload: the base-model encoder self-attention, bf16, batch 32,
 N = 512, d_model = 512, h = 8, d_k = 64, no mask; a step is one mha_forward
 (Q/K/V projections, attention, W^O). Attention-only workloads
-(--workload decoder|cross|long) time one attention_forward per step.
+(--workload decoder|cross|long) time one attention_forward per step;
+--workload decode times one attention_decode (one query per (batch, head)
+against a paged K/V cache), reported against the HBM roofline.
 
 Prints ONE JSON line. `value` is algorithmic TFLOP/s of the step (FLOPs =
 4*B*H*d*unmasked pairs for attention, 2*m*n*k per projection) with inputs
@@ -42,6 +44,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "attention": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_bf16.hip"),
     "linear": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "linear_bf16.hip"),
+    "decode": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "decode.hip"),
 }
 
 
@@ -103,7 +106,12 @@ def cpu_baseline(w, inputs, min_seconds=10.0, max_seconds=30.0):
     import oracle
     info = threadpoolctl.threadpool_info()
     threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
-    if w.kind == "layer":
+    if w.kind == "decode":
+        fn = lambda: oracle.decode_ref(inputs["q"].value, inputs["k"].value, inputs["v"].value, w.kv_lengths())
+        flops = w.attention_flops()
+        sample = (f"the full workload ({w.batch * w.heads} (batch, head) pairs against their cached keys), "
+                  "oracle.decode_ref in float64 on the logical (unpaged) cache")
+    elif w.kind == "layer":
         names = {"ln1_gamma": "ln1_g", "ln1_beta": "ln1_b", "ln2_gamma": "ln2_g", "ln2_beta": "ln2_b"}
         params = {names.get(k, k): v.value for k, v in inputs.items() if k != "x"}
         fn = lambda: oracle.encoder_layer_ref(inputs["x"].value, params, w.heads)
@@ -146,7 +154,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="encoder",
-                    help="encoder | tiny | decoder | cross | long | padded | layer")
+                    help="encoder | tiny | decoder | cross | long | padded | layer | decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the long causal attention line")
     ap.add_argument("--calib-copy", action="store_true",
@@ -173,7 +181,33 @@ def main():
     result = {}
     lens = w.kv_lengths()
     kv_len = None if lens is None else torch.from_numpy(lens).to(dev)
-    if w.kind == "layer":
+    if w.kind == "decode":
+        table_np, num_pages = w.pages()
+        q = torch_tensor(inputs["q"], dev)
+        kp = torch_tensor(workloads.paged_pool(inputs["k"], table_np, lens, w.page_size, num_pages), dev)
+        vp = torch_tensor(workloads.paged_pool(inputs["v"], table_np, lens, w.page_size, num_pages), dev)
+        table = torch.from_numpy(table_np).to(dev)
+        esz = q.element_size()
+        pool_bytes = 2 * kp.numel() * esz
+        n_sets = max(1, math.ceil(ROTATE_BYTES / pool_bytes))
+        pools = [(kp, vp)] + [(kp.clone(), vp.clone()) for _ in range(n_sets - 1)]
+        outs = [torch.empty_like(q) for _ in range(n_sets)]
+        need = mha.attention_decode_workspace_size(w.batch, w.heads, w.d_k, w.n_k)
+        work = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def step(i):
+            ki, vi = pools[i % n_sets]
+            mha.attention_decode(q, ki, vi, kv_len, block_table=table, out=outs[i % n_sets], workspace=work)
+
+        step(0)
+        torch.cuda.synchronize()
+        flops_step = w.attention_flops()
+        # the step is the decode itself: the split kernel and the merge of the splits
+        dom_fn, dom_flops, dom_name = step, flops_step, "decode_split_kernel"
+        # algorithmic bytes: every visible cached key and value row, q in, o out
+        dom_bytes = (2 * w.heads * int(lens.astype(np.int64).sum()) * w.d_k + 2 * w.batch * w.heads * w.d_k) * esz
+        get_out = lambda: outs[0]
+    elif w.kind == "layer":
         dm, ff = w.d_model, w.d_ff
         x = torch_tensor(inputs["x"], dev)
         params = {k: torch_tensor(v, dev) for k, v in inputs.items() if k != "x"}
@@ -272,12 +306,22 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     launch_desc = f"{dom_name}:{w.name}"
-    roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic_for("linear" if dom_name.startswith("linear") else "attention", launch_desc),
-                "algorithmic_bytes": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
-                "achieved_gbps": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1)}
-    log(f"dominant kernel {dom_name}: {dom_ms * 1e3:.1f} us, {achieved:.1f} TFLOP/s")
+    src_key = "linear" if dom_name.startswith("linear") else "decode" if dom_name.startswith("decode") else "attention"
+    gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
+    if w.kind == "decode":
+        # one query row: 2 flops per byte-pair of K/V, far below the MFMA ridge -- HBM-bound
+        roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(gbps, 1), "peak": HBM_GBPS,
+                    "unit": "GB/s", "frac": round(gbps / HBM_GBPS, 4),
+                    "traffic": traffic_for(src_key, launch_desc), "algorithmic_bytes": dom_bytes,
+                    "avg_launch_us": round(dom_ms * 1e3, 2), "launches_per_step": 2,
+                    "achieved_tflops": round(achieved, 3)}
+    else:
+        roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": traffic_for(src_key, launch_desc),
+                    "algorithmic_bytes": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
+                    "achieved_gbps": round(gbps, 1)}
+    log(f"dominant kernel {dom_name}: {dom_ms * 1e3:.1f} us, {achieved:.1f} TFLOP/s, {gbps:.0f} GB/s")
 
     secondary = None
     if not args.no_secondary and w.name != workloads.get("long").name:
@@ -318,11 +362,16 @@ def main():
            "d_k": w.d_k, "causal": w.causal,
            "step": {"mha": "mha_forward: QKV projections + attention + W^O",
                     "layer": "encoder_layer_forward: attention sub-layer + residual LayerNorm + FFN + residual "
-                             "LayerNorm"}.get(w.kind, "attention_forward")}
+                             "LayerNorm",
+                    "decode": "attention_decode: one query per (batch, head) against the paged K/V cache "
+                              "(split kernel + merge)"}.get(w.kind, "attention_forward")}
     if w.kind in ("mha", "layer"):
         cfg["d_model"] = w.d_model
     if w.kind == "layer":
         cfg["d_ff"] = w.d_ff
+    if w.kind == "decode":
+        cfg["page_size"] = w.page_size
+        cfg["cache_capacity"] = w.n_k
     if lens is not None:
         cfg["kv_len"] = (f"per-batch key lengths uniform in [{w.kv_len_range[0]}, {w.kv_len_range[1]}] "
                          f"(seeded; mean {float(lens.mean()):.1f})")

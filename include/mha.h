@@ -235,6 +235,69 @@ mha_status encoder_layer_forward(const void* x, const mha_encoder_weights* weigh
                                  int heads, int d_ff, float eps, mha_dtype dtype, int causal,
                                  const int32_t* kv_len, void* stream);
 
+/*
+ * attention_decode -- one decoding step against a key/value cache: for every
+ * (batch, head) the newest position's query attends to the first kv_len[b]
+ * cached keys and values,
+ *   o[b,h,:] = sum_{j < kv_len[b]} softmax_j( scale * q[b,h,:] . K[b,h,j,:] ) V[b,h,j,:].
+ * This is the last row of causal attention over the sequence so far: a
+ * decoder generates left to right and its masked self-attention covers the
+ * tokens generated so far ("How Transformers Work" (worksonmygpu.com), "What
+ * changed since 2017"; "The Transformer" (hoshank.vercel.app), "The
+ * Breakthrough"; the mask: "The Transformer" (rayaq.ca), "Masks: who may look
+ * at whom"). The same page names PagedAttention as how K and V are stored
+ * when serving; the pages give no layout, so the cache here may be kept in
+ * fixed-size pages reached through a per-sequence page table (a reading).
+ *
+ * q, o: (batch, heads, d) contiguous, of `dtype`, device memory.
+ * cache: HOST pointer to an mha_kv_cache describing two DEVICE pools, k and
+ *   v, of identical geometry. Element e of head h at (page, slot) is at
+ *     page * page_stride + slot * row_stride + h * head_stride + e
+ *   (element strides, non-negative, multiples of 8 (bf16) or 4 (f32); the
+ *   last dimension contiguous). Key j of sequence b is at
+ *     (page, slot) = (block_table[b * max_pages + j / page_size], j % page_size)
+ *   when block_table (DEVICE, int32, (batch, max_pages)) is non-NULL, and at
+ *   (page, slot) = (b, j) otherwise, so a plain (batch, max_len, heads, d)
+ *   cache has strides {max_len*heads*d, heads*d, d} and a (batch, heads,
+ *   max_len, d) one {heads*max_len*d, d, max_len*d}. page_size, max_pages
+ *   and num_pages are read only with a block table.
+ *   max_len: capacity of one sequence in keys (<= page_size * max_pages with
+ *   a table); kv_len values are clamped to [0, max_len].
+ *   A table entry read for a key below kv_len[b] that lies outside
+ *   [0, num_pages) is not dereferenced: that (batch item, head)'s o and lse
+ *   become NaN. Entries for keys at or past kv_len[b] are never read.
+ * kv_len: DEVICE, `batch` int32. A length of 0 gives o = 0 and lse = -inf.
+ * lse: NULL, or DEVICE fp32 (batch, heads): natural-log sum of exp(scores).
+ * scale: multiplies the scores (1/sqrt(d) for the pages' attention); finite.
+ * workspace: DEVICE scratch of at least attention_decode_workspace_size()
+ *   bytes, 16-byte aligned, owned by the caller (partial softmax states of
+ *   the key splits).
+ * Supported: d in {16, 32, 64, 128}, bf16 or f32 (MHA_ERR_UNSUPPORTED
+ *   otherwise); max_len <= 16776960 (65535 splits of 256 keys).
+ * bf16: scores, softmax and the weighted sum are fp32 (no rounding of the
+ *   weights); o is rounded to bf16 once.
+ * Launches, both on `stream`: one workgroup per (batch, head, 256-key split)
+ *   that holds a key, then one merge of the splits per (batch, head).
+ */
+typedef struct mha_kv_cache {
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  int64_t page_stride;
+  int64_t row_stride;
+  int64_t head_stride;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t max_len;
+} mha_kv_cache;
+
+size_t attention_decode_workspace_size(int batch, int heads, int d, int max_len);
+
+mha_status attention_decode(const void* q, const mha_kv_cache* cache, const int32_t* kv_len, void* o,
+                            float* lse, void* workspace, size_t workspace_bytes, int batch, int heads,
+                            int d, mha_dtype dtype, float scale, void* stream);
+
 /* Static English name of a status code (never NULL). */
 const char* mha_status_string(mha_status status);
 

@@ -273,10 +273,12 @@ def gather_pages(pool: np.ndarray, block_table, page_size: int, length: int) -> 
 def decode_ref(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, kv_len, *, scale: float | None = None):
     """One decoding step: each (batch, head) query attends to the first
     kv_len[b] cached keys and values -- the newest row of causal attention,
-    where position i sees keys j <= i ("How Transformers Work", the decoder
-    generating left to right; "The Transformer" (rayaq.ca), "Masks: who may
-    look at whom"). q: (B, H, d); k_cache, v_cache: (B, H, N_max, d).
-    Returns (O (B, H, d), lse (B, H)); a length of 0 gives O = 0, lse = -inf."""
+    where position i sees keys j <= i: decoder-only models generate left to
+    right ("How Transformers Work" (worksonmygpu.com), "What changed since
+    2017"), the decoder's masked self-attention covers the tokens generated so
+    far ("The Transformer" (hoshank.vercel.app), "The Breakthrough"), and the
+    causal mask is "The Transformer" (rayaq.ca), "Masks: who may look at
+    whom". q: (B, H, d); k_cache, v_cache: (B, H, N_max, d). Returns (O (B, H, d), lse (B, H)); a length of 0 gives O = 0, lse = -inf."""
     q = np.asarray(q, dtype=np.float64)
     o, _, lse = attention_ref(q[:, :, None, :], k_cache, v_cache, scale=scale, kv_len=kv_len)
     return o[:, :, 0, :], lse[:, :, 0]

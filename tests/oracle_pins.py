@@ -585,8 +585,10 @@ def check_encoder_layer_params():
 def check_decode_is_last_causal_row(decode, attn):
     """Generating left to right, the newest token's query sees every cached key
     up to and including its own position: one decoding step equals the last row
-    of causal attention over the sequence so far ("How Transformers Work";
-    "The Transformer" (rayaq.ca), "Masks: who may look at whom")."""
+    of causal attention over the sequence so far ("How Transformers Work"
+    (worksonmygpu.com), "What changed since 2017"; "The Transformer"
+    (hoshank.vercel.app), "The Breakthrough"; "The Transformer" (rayaq.ca),
+    "Masks: who may look at whom")."""
     q, k, v = _qkv(60, B=3, H=2, nq=9, nk=9, d=4)
     full, _, full_lse = attn(q, k, v, causal=True)
     for L in (1, 5, 9):

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     fns = header_functions()
     assert {"attention_forward", "attention_forward_padded", "mha_forward", "mha_forward_padded",
             "mha_forward_workspace_size", "linear_forward", "encoder_layer_workspace_size",
-            "encoder_layer_forward", "mha_status_string", "mha_last_error", "mha_version"} == set(fns)
+            "encoder_layer_forward", "attention_decode_workspace_size", "attention_decode",
+            "mha_status_string", "mha_last_error", "mha_version"} == set(fns)
     assert set(fns) == set(_lib.SIGNATURES), "binding signatures out of sync with include/mha.h"
 
 
@@ -238,3 +239,53 @@ def test_encoder_layer_workspace_size(lib):
     B, n, dm, ff = 32, 512, 512, 2048
     assert lib.encoder_layer_workspace_size(B, n, dm, 8, ff, 1) == 4 * r(B * n * dm * 2) + r(B * n * ff * 2)
     assert lib.encoder_layer_workspace_size(B, n, dm, 8, 0, 1) == 0
+
+
+def cache(k=FAKE, v=FAKE, table=None, ps=8 * 64, rs=64, hs=4096 * 8 * 64 // 8, page_size=0, max_pages=0, num_pages=0,
+          max_len=4096):
+    return _lib.KVCache(k, v, table, ps, rs, hs, page_size, max_pages, num_pages, max_len)
+
+
+def dec(lib, c=None, q=FAKE, kv_len=FAKE, o=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 40, B=2, H=8, d=64,
+        dtype=_lib.MHA_BF16, scale=0.125):
+    c = cache() if c is None else c
+    return lib.attention_decode(q, ctypes.byref(c) if c is not False else None, kv_len, o, lse, ws, ws_bytes, B, H,
+                                d, dtype, scale, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(c=False), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(kv_len=None), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(ws=None), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(c=cache(v=None)), _lib.MHA_ERR_INVALID_ARG, "cache->v"),
+    (dict(B=0), _lib.MHA_ERR_INVALID_ARG, ">= 1"),
+    (dict(c=cache(max_len=0)), _lib.MHA_ERR_INVALID_ARG, ">= 1"),
+    (dict(dtype=7), _lib.MHA_ERR_INVALID_ARG, "dtype"),
+    (dict(scale=float("inf")), _lib.MHA_ERR_INVALID_ARG, "scale"),
+    (dict(d=48), _lib.MHA_ERR_UNSUPPORTED, "decode supports d"),
+    (dict(c=cache(rs=-64)), _lib.MHA_ERR_INVALID_ARG, "negative"),
+    (dict(c=cache(hs=12)), _lib.MHA_ERR_INVALID_ARG, "multiple of 8"),
+    (dict(c=cache(k=MIS)), _lib.MHA_ERR_INVALID_ARG, "16-byte"),
+    (dict(o=MIS), _lib.MHA_ERR_INVALID_ARG, "16-byte"),
+    (dict(kv_len=FAKE + 2), _lib.MHA_ERR_INVALID_ARG, "4-byte"),
+    (dict(lse=FAKE + 2), _lib.MHA_ERR_INVALID_ARG, "4-byte"),
+    (dict(c=cache(table=FAKE + 2, page_size=16, max_pages=256, num_pages=10)), _lib.MHA_ERR_INVALID_ARG, "4-byte"),
+    (dict(c=cache(table=FAKE, page_size=0, max_pages=256, num_pages=10)), _lib.MHA_ERR_INVALID_ARG, "page_size"),
+    (dict(c=cache(table=FAKE, page_size=16, max_pages=256, num_pages=0)), _lib.MHA_ERR_INVALID_ARG, "num_pages"),
+    (dict(c=cache(table=FAKE, page_size=16, max_pages=255, num_pages=10)), _lib.MHA_ERR_INVALID_ARG, "exceeds"),
+    (dict(c=cache(max_len=65536 * 256)), _lib.MHA_ERR_UNSUPPORTED, "max_len"),
+    (dict(ws_bytes=1000), _lib.MHA_ERR_WORKSPACE, "required"),
+])
+def test_decode_validation(lib, kw, status, needle):
+    assert dec(lib, **kw) == status
+    assert needle in lib.mha_last_error().decode()
+
+
+def test_decode_workspace_size(lib):
+    def r(x):
+        return (x + 255) // 256 * 256
+    for B, H, d, n in ((64, 8, 64, 4096), (3, 5, 128, 257), (1, 1, 16, 1)):
+        parts = B * H * ((n + 255) // 256)
+        assert lib.attention_decode_workspace_size(B, H, d, n) == r(parts * 8) + r(parts * d * 4)
+    assert lib.attention_decode_workspace_size(1, 1, 64, 0) == 0

@@ -11,11 +11,11 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import (ENCODER_WEIGHT_NAMES, EncoderWeights, MHA_BF16, MHA_ERR_HIP, MHA_ERR_INVALID_ARG,
+from ._lib import (ENCODER_WEIGHT_NAMES, EncoderWeights, KVCache, MHA_BF16, MHA_ERR_HIP, MHA_ERR_INVALID_ARG,
                    MHA_ERR_UNSUPPORTED,
                    MHA_ERR_WORKSPACE, MHA_F32, MHA_OK, LIB_PATH, MHAError, check, load, strides3)
 
-__all__ = ["attention_forward", "encoder_layer_forward", "encoder_layer_workspace_size", "linear_forward",
+__all__ = ["attention_decode", "attention_decode_workspace_size", "attention_forward", "encoder_layer_forward", "encoder_layer_workspace_size", "linear_forward",
            "mha_forward", "mha_forward_workspace_size",
            "MHAError", "MHA_F32", "MHA_BF16", "LIB_PATH", "load"]
 
@@ -229,3 +229,72 @@ def encoder_layer_forward(x, weights: dict, heads: int, *, eps: float = 1e-5, ca
                                        float(eps), code, int(bool(causal)), kvp, _stream_handle(dev, stream))
     check(st)
     return out
+
+
+def attention_decode_workspace_size(batch: int, heads: int, d: int, max_len: int) -> int:
+    """Bytes of device workspace attention_decode needs (0 for invalid sizes)."""
+    return int(load().attention_decode_workspace_size(batch, heads, d, max_len))
+
+
+def attention_decode(q, k_cache, v_cache, kv_len, *, block_table=None, scale: float | None = None, out=None,
+                     return_lse: bool = False, workspace=None, stream=None):
+    """One decoding step: q (B, H, d) attends to the first kv_len[b] cached keys.
+
+    k_cache, v_cache: 4-D tensors (pages, slots, H, d) with a contiguous last
+    dimension and identical shape and strides; their strides are the cache
+    geometry passed to the library.
+      - block_table None: page b is sequence b (pages == B) and slot j is its
+        key j, so a (B, max_len, H, d) cache is passed as is and a
+        (B, H, max_len, d) one as .transpose(1, 2).
+      - block_table: int32 device tensor (B, max_pages); key j of sequence b
+        is in page block_table[b, j // slots] at slot j % slots.
+    kv_len: int32 device tensor (B,). Returns out (B, H, d), and the fp32
+    log-sum-exp (B, H) when return_lse is set.
+    """
+    torch = _torch()
+    dev = _require_device(q, k_cache, v_cache)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous (B, H, d) tensor")
+    B, H, d = q.shape
+    if k_cache.dim() != 4 or tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must be 4-D (pages, slots, H, d) with equal shapes and strides")
+    pages, slots, hc, dc = k_cache.shape
+    if (hc, dc) != (H, d) or k_cache.stride(3) != 1:
+        raise ValueError(f"cache heads/width {(hc, dc)} must match q's {(H, d)} with a contiguous last dimension")
+    table_p = None
+    page_size = max_pages = num_pages = 0
+    if block_table is None:
+        if pages != B:
+            raise ValueError(f"without a block table the cache's first dimension must be the batch ({B})")
+        max_len = slots
+    else:
+        if not isinstance(block_table, torch.Tensor) or block_table.dtype != torch.int32:
+            raise TypeError("block_table must be an int32 tensor")
+        if not block_table.is_cuda or block_table.device != dev:
+            raise ValueError("block_table must live on the same GPU as the inputs")
+        if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+            raise ValueError(f"block_table must be a contiguous ({B}, max_pages) tensor")
+        page_size, max_pages, num_pages = slots, block_table.shape[1], pages
+        max_len = page_size * max_pages
+        table_p = block_table.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=q.dtype, device=dev)
+    _require_device(q, out)
+    if tuple(out.shape) != (B, H, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B, H, d) tensor")
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev) if return_lse else None
+    lib = load()
+    need = int(lib.attention_decode_workspace_size(B, H, d, max_len))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    cache = KVCache(k_cache.data_ptr(), v_cache.data_ptr(), table_p, k_cache.stride(0), k_cache.stride(1),
+                    k_cache.stride(2), page_size, max_pages, num_pages, max_len)
+    with torch.cuda.device(dev):
+        st = lib.attention_decode(q.data_ptr(), ctypes.byref(cache), _kv_len_arg(kv_len, B, dev), out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), B, H, d, _dtype_code(q),
+                                  float(scale), _stream_handle(dev, stream))
+    check(st)
+    return (out, lse) if return_lse else out

@@ -27,6 +27,14 @@ class EncoderWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ENCODER_WEIGHT_NAMES]
 
 
+class KVCache(ctypes.Structure):
+    """mha_kv_cache of include/mha.h: the cache pools and their geometry."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("page_stride", ctypes.c_int64), ("row_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_len", ctypes.c_int32)]
+
+
 # name -> (restype, argtypes); must match include/mha.h
 SIGNATURES = {
     "attention_forward": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int,
@@ -45,6 +53,9 @@ SIGNATURES = {
     "encoder_layer_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int, _int, _int]),
     "encoder_layer_forward": (_int, [_vp, ctypes.POINTER(EncoderWeights), _vp, _vp, ctypes.c_size_t, _int, _int,
                                      _int, _int, _int, ctypes.c_float, _int, _int, _vp, _vp]),
+    "attention_decode_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int]),
+    "attention_decode": (_int, [_vp, ctypes.POINTER(KVCache), _vp, _vp, _vp, _vp, ctypes.c_size_t, _int, _int,
+                                _int, _int, ctypes.c_float, _vp]),
     "mha_status_string": (ctypes.c_char_p, [_int]),
     "mha_last_error": (ctypes.c_char_p, []),
     "mha_version": (_int, []),

@@ -55,11 +55,33 @@ struct AddNormArgs {
   float eps;
 };
 
+// One decoding step: query (batch, heads, d) against the first kv_len[b] keys
+// and values of a cache (see decode.hip for the addressing). Strides in
+// elements. Partial softmax states of the key splits go to part_ml / part_o.
+constexpr int kDecodeChunk = 256;  // keys per split
+struct DecodeArgs {
+  const void* q;  // (batch, heads, d) contiguous
+  const void* k;
+  const void* v;
+  const int* kv_len;       // (batch), clamped to [0, max_len]
+  const int* block_table;  // nullable, (batch, max_pages)
+  int page_size, max_pages, num_pages, max_len;
+  int64_t page_stride, row_stride, head_stride;
+  void* o;       // (batch, heads, d) contiguous
+  float* lse;    // nullable, (batch, heads)
+  float* part_ml;  // (batch * heads, splits, 2): running max (base 2) and sum
+  float* part_o;   // (batch * heads, splits, d): unnormalised output
+  int batch, heads, d, splits;
+  float scale;
+};
+
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_add_layernorm_bf16(const AddNormArgs& a, hipStream_t stream);
 hipError_t launch_add_layernorm_f32(const AddNormArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace mha

@@ -335,6 +335,89 @@ mha_status encoder_layer_impl(const void* x, const mha_encoder_weights* wts, voi
   return run_add_norm(mha::AddNormArgs{h, t2, wts->ln2_gamma, wts->ln2_beta, out, rows, d_model, eps}, dtype, st);
 }
 
+// Decode workspace: per (batch, head, split) the running max and sum, then
+// the unnormalised output row, both fp32.
+bool decode_ws_layout(int batch, int heads, int d, int max_len, size_t* o_off, size_t* total) {
+  const int64_t splits = ((int64_t)max_len + mha::kDecodeChunk - 1) / mha::kDecodeChunk;
+  const unsigned __int128 parts = (unsigned __int128)batch * heads * splits;
+  const unsigned __int128 tot = parts * (2 + d) * 4 + 2 * kAlign;
+  if (tot > ((unsigned __int128)1 << 62)) return false;
+  *o_off = round_up((size_t)(parts * 2 * 4));
+  *total = *o_off + round_up((size_t)(parts * d * 4));
+  return true;
+}
+
+mha_status decode_impl(const void* q, const mha_kv_cache* cache, const int32_t* kv_len, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes, int batch, int heads, int d, mha_dtype dtype,
+                       float scale, void* stream) {
+  if (!q || !cache || !kv_len || !o || !workspace)
+    return fail(MHA_ERR_INVALID_ARG, "q, cache, kv_len, o and workspace must be non-null");
+  if (!cache->k || !cache->v) return fail(MHA_ERR_INVALID_ARG, "cache->k and cache->v must be non-null");
+  if (batch < 1 || heads < 1 || d < 1 || cache->max_len < 1)
+    return fail(MHA_ERR_INVALID_ARG, "sizes must be >= 1 (batch=%d heads=%d d=%d max_len=%d)", batch, heads, d,
+                cache->max_len);
+  if (!valid_dtype(dtype)) return fail(MHA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!isfinite(scale)) return fail(MHA_ERR_INVALID_ARG, "scale must be finite");
+  if (!f32_head_width(d))
+    return fail(MHA_ERR_UNSUPPORTED, "decode supports d in {16, 32, 64, 128} (got %d)", d);
+  const int vec = vec_elems(dtype);
+  const int64_t strides[3] = {cache->page_stride, cache->row_stride, cache->head_stride};
+  const char* names[3] = {"page_stride", "row_stride", "head_stride"};
+  for (int i = 0; i < 3; ++i) {
+    if (strides[i] < 0) return fail(MHA_ERR_INVALID_ARG, "cache %s is negative", names[i]);
+    if (strides[i] % vec)
+      return fail(MHA_ERR_INVALID_ARG, "cache %s (%lld) must be a multiple of %d elements", names[i],
+                  (long long)strides[i], vec);
+  }
+  if (!aligned16(q) || !aligned16(cache->k) || !aligned16(cache->v) || !aligned16(o) || !aligned16(workspace))
+    return fail(MHA_ERR_INVALID_ARG, "q, cache->k, cache->v, o and workspace must be 16-byte aligned");
+  if (!aligned4(kv_len) || (lse && !aligned4(lse)))
+    return fail(MHA_ERR_INVALID_ARG, "kv_len and lse must be 4-byte aligned");
+  if (cache->block_table) {
+    if (!aligned4(cache->block_table)) return fail(MHA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    if (cache->page_size < 1 || cache->max_pages < 1 || cache->num_pages < 1)
+      return fail(MHA_ERR_INVALID_ARG, "page_size, max_pages and num_pages must be >= 1 with a block table");
+    if ((int64_t)cache->page_size * cache->max_pages < cache->max_len)
+      return fail(MHA_ERR_INVALID_ARG, "max_len (%d) exceeds page_size * max_pages (%lld)", cache->max_len,
+                  (long long)cache->page_size * cache->max_pages);
+  }
+  const int64_t bhs = (int64_t)batch * heads;
+  const int64_t splits = ((int64_t)cache->max_len + mha::kDecodeChunk - 1) / mha::kDecodeChunk;
+  if (bhs > INT32_MAX || splits > 65535)
+    return fail(MHA_ERR_UNSUPPORTED, "too many (batch, head) pairs or max_len too large for one launch");
+  size_t o_off = 0, total = 0;
+  if (!decode_ws_layout(batch, heads, d, cache->max_len, &o_off, &total))
+    return fail(MHA_ERR_INVALID_ARG, "sizes overflow");
+  if (workspace_bytes < total)
+    return fail(MHA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, total);
+
+  mha::DecodeArgs a = {};
+  a.q = q;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.kv_len = kv_len;
+  a.block_table = cache->block_table;
+  a.page_size = cache->page_size;
+  a.max_pages = cache->max_pages;
+  a.num_pages = cache->num_pages;
+  a.max_len = cache->max_len;
+  a.page_stride = cache->page_stride;
+  a.row_stride = cache->row_stride;
+  a.head_stride = cache->head_stride;
+  a.o = o;
+  a.lse = lse;
+  a.part_ml = static_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_off);
+  a.batch = batch;
+  a.heads = heads;
+  a.d = d;
+  a.splits = (int)splits;
+  a.scale = scale;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == MHA_BF16 ? mha::launch_decode_bf16(a, st) : mha::launch_decode_f32(a, st);
+  return hip_status(e, "decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,7 +435,7 @@ const char* mha_status_string(mha_status s) {
 
 const char* mha_last_error(void) { return g_last_error.c_str(); }
 
-int mha_version(void) { return 200; }
+int mha_version(void) { return 300; }
 
 mha_status attention_forward(const void* q, const void* k, const void* v, void* o, int batch, int heads,
                              int n_q, int n_k, int d_k, int d_v, const int64_t q_strides[3],
@@ -449,6 +532,23 @@ mha_status encoder_layer_forward(const void* x, const mha_encoder_weights* weigh
                               causal, kv_len, stream);
   } catch (...) {
     return fail(MHA_ERR_HIP, "internal error in encoder_layer_forward");
+  }
+}
+
+size_t attention_decode_workspace_size(int batch, int heads, int d, int max_len) {
+  if (batch < 1 || heads < 1 || d < 1 || max_len < 1) return 0;
+  size_t o_off = 0, total = 0;
+  if (!decode_ws_layout(batch, heads, d, max_len, &o_off, &total)) return 0;
+  return total;
+}
+
+mha_status attention_decode(const void* q, const mha_kv_cache* cache, const int32_t* kv_len, void* o, float* lse,
+                            void* workspace, size_t workspace_bytes, int batch, int heads, int d, mha_dtype dtype,
+                            float scale, void* stream) {
+  try {
+    return decode_impl(q, cache, kv_len, o, lse, workspace, workspace_bytes, batch, heads, d, dtype, scale, stream);
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in attention_decode");
   }
 }
 

@@ -30,7 +30,8 @@ import numpy as np
 class Workload:
     name: str
     kind: str            # "mha": projections + attention + W^O;  "attn": attention core only;
-                         # "layer": a whole encoder layer (attention sub-layer, FFN, two residual norms)
+                         # "layer": a whole encoder layer (attention sub-layer, FFN, two residual norms);
+                         # "decode": one query per (batch, head) against a K/V cache of n_k slots
     dtype: str           # "f32" or "bf16": the stored type of every tensor
     batch: int
     heads: int
@@ -43,6 +44,7 @@ class Workload:
     oracle_rows: int = 0  # >0: the oracle checks this many sampled query positions
     kv_len_range: tuple = ()  # (lo, hi): per-batch key lengths drawn uniformly in [lo, hi] (padding mask)
     d_ff: int = 0        # layer workloads only: FFN inner width
+    page_size: int = 0   # decode workloads: key slots per cache page (0: one contiguous cache per sequence)
 
     def kv_lengths(self):
         """Per-batch key lengths of a padded workload (None if unpadded), from
@@ -52,6 +54,11 @@ class Workload:
             return None
         lo, hi = self.kv_len_range
         return np.random.default_rng(2000 + self.seed).integers(lo, hi + 1, size=self.batch).astype(np.int32)
+
+    def pages(self):
+        """(block_table, num_pages) of a paged decode workload: page_table over
+        the key lengths with its own generator seed 3000 + seed."""
+        return page_table(self.kv_lengths(), self.page_size, self.n_k // self.page_size, seed=3000 + self.seed)
 
     @property
     def d_v(self) -> int:
@@ -120,6 +127,10 @@ WORKLOADS: dict[str, Workload] = {
         # one whole encoder layer of the base model (d_ff = 2048)
         Workload("base_encoder_layer_bf16_b32_n512", "layer", "bf16", batch=32, heads=8,
                  n_q=512, n_k=512, d_k=64, causal=False, seed=7, d_model=512, d_ff=2048),
+        # one decoding step of the base model (8 heads of 64) for 64 sequences against a
+        # paged K/V cache of 16-slot pages; cached lengths uniform in [1024, 4096]
+        Workload("decode_paged_bf16_b64_h8_kv4096", "decode", "bf16", batch=64, heads=8,
+                 n_q=1, n_k=4096, d_k=64, causal=False, seed=8, kv_len_range=(1024, 4096), page_size=16),
     ]
 }
 
@@ -132,6 +143,7 @@ ALIASES = {
     "long": "long_causal_bf16_b2_h16_n8192",
     "padded": "base_encoder_padded_mha_bf16_b32_n512",
     "layer": "base_encoder_layer_bf16_b32_n512",
+    "decode": "decode_paged_bf16_b64_h8_kv4096",
 }
 
 
@@ -149,9 +161,13 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     occur in these inputs.
     """
     f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    bias = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
-    return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+    u = f.view(np.uint32)
+    # finite inputs: u + bias stays below 2^32 (the largest finite pattern is 0xFF7FFFFF)
+    bias = (u >> np.uint32(16)) & np.uint32(1)
+    bias += np.uint32(0x7FFF)
+    bias += u
+    bias >>= np.uint32(16)
+    return bias.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -197,6 +213,7 @@ def make_inputs(w: Workload, *, v_ones: bool = False) -> dict[str, Stored]:
           as the query, key and value input.
     layer: x (B, N, d_model), then encoder_params(d_model, d_ff, seed=100 + seed).
     attn: Q (B, H, N_q, d), K (B, H, N_k, d), V (B, H, N_k, d).
+    decode: Q (B, H, d), then the logical caches K (B, H, N_k, d), V (B, H, N_k, d).
     v_ones replaces V by all ones after drawing (row-sum checks); the draws
     themselves are unchanged so Q and K stay identical to the plain run.
     """
@@ -213,7 +230,8 @@ def make_inputs(w: Workload, *, v_ones: bool = False) -> dict[str, Stored]:
         for name in ("wq", "wk", "wv", "wo"):
             out[name] = store(rng.standard_normal((dm, dm)) * s, w.dtype)
         return out
-    out["q"] = store(rng.standard_normal((w.batch, w.heads, w.n_q, w.d_k)), w.dtype)
+    qshape = (w.batch, w.heads, w.d_k) if w.kind == "decode" else (w.batch, w.heads, w.n_q, w.d_k)
+    out["q"] = store(rng.standard_normal(qshape), w.dtype)
     out["k"] = store(rng.standard_normal((w.batch, w.heads, w.n_k, w.d_k)), w.dtype)
     v = rng.standard_normal((w.batch, w.heads, w.n_k, w.d_v))
     if v_ones:
@@ -245,6 +263,43 @@ def encoder_params(d_model: int, d_ff: int, dtype: str, seed: int) -> dict[str, 
             z = 0.1 * z
         out[name] = store(z, dtype)
     return out
+
+
+def page_table(lengths, page_size: int, max_pages: int, seed: int, spare: int = 0):
+    """A shuffled page assignment for a paged cache.
+
+    Sequence b owns ceil(lengths[b] / page_size) pages; all owned pages, plus
+    `spare` unowned ones, are numbered 0..num_pages-1 in a random order drawn
+    from ``default_rng(seed)`` (a permutation), so logically adjacent pages are
+    physically scattered. Table entries past a sequence's own pages are -1.
+    Returns (table (B, max_pages) int32, num_pages)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    need = (lengths + page_size - 1) // page_size
+    if np.any(need > max_pages):
+        raise ValueError("a sequence needs more pages than a table row holds")
+    num_pages = int(need.sum()) + spare
+    perm = np.random.default_rng(seed).permutation(num_pages).astype(np.int32)
+    table = np.full((len(lengths), max_pages), -1, dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[pos:pos + n]
+        pos += int(n)
+    return table, num_pages
+
+
+def paged_pool(stored: Stored, table, lengths, page_size: int, num_pages: int) -> Stored:
+    """Move a logical cache (B, H, N, d) into a page pool (num_pages, page_size,
+    H, d) laid out by `table` (rows only move; slots no sequence owns stay 0).
+    The returned Stored carries the raw pool only (value is None)."""
+    raw = stored.raw
+    B, H, N, d = raw.shape
+    pool = np.zeros((num_pages, page_size, H, d), dtype=raw.dtype)
+    for b in range(B):
+        n_pages = (int(lengths[b]) + page_size - 1) // page_size
+        for i in range(n_pages):
+            rows = raw[b, :, i * page_size:(i + 1) * page_size, :]     # (H, <=page_size, d)
+            pool[table[b, i], :rows.shape[1]] = rows.transpose(1, 0, 2)
+    return Stored(None, stored.dtype, pool)
 
 
 def random_tensor(shape, dtype: str, seed: int, scale: float = 1.0) -> Stored:
