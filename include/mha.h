@@ -271,13 +271,15 @@ mha_status encoder_layer_forward(const void* x, const mha_encoder_weights* weigh
  * scale: multiplies the scores (1/sqrt(d) for the pages' attention); finite.
  * workspace: DEVICE scratch of at least attention_decode_workspace_size()
  *   bytes, 16-byte aligned, owned by the caller (partial softmax states of
- *   the key splits).
+ *   the key splits); no initial contents needed. Calls that overlap on one
+ *   workspace race.
  * Supported: d in {16, 32, 64, 128}, bf16 or f32 (MHA_ERR_UNSUPPORTED
  *   otherwise); max_len <= 16776960 (65535 splits of 256 keys).
  * bf16: scores, softmax and the weighted sum are fp32 (no rounding of the
  *   weights); o is rounded to bf16 once.
- * Launches, both on `stream`: one workgroup per (batch, head, 256-key split)
- *   that holds a key, then one merge of the splits per (batch, head).
+ * Launches, both on `stream`: a workgroup per (batch, head, 256-key split)
+ *   that holds a key (a sequence of one split, or of none, is finished
+ *   there), then one merge of the splits per (batch, head).
  */
 typedef struct mha_kv_cache {
   const void* k;

@@ -4,9 +4,9 @@ One query row per (batch, head) against the first kv_len[b] cached keys, with
 the cache contiguous (both (B, N, H, d) and (B, H, N, d) layouts, passed by
 strides) or paged through a shuffled page table. Bars: the attention bars,
 max-abs 1e-4 (fp32) / 2e-2 (bf16) on unit-variance inputs, and the
-log-sum-exp within LSE_TOL. Lengths cover 0, 1, split edges (256, 257, 512)
-and ragged tails; the paged cases use page sizes that do and do not divide the
-256-key split.
+log-sum-exp within 1e-5. Lengths cover 0, 1, split edges (256, 257, 512),
+ragged tails and caches of up to 79 splits; the paged cases use page sizes
+that do and do not divide the 256-key split.
 """
 import numpy as np
 import pytest
@@ -14,7 +14,7 @@ import pytest
 import oracle
 import transformer_scaled_dot_mha_amd as mha
 import workloads
-from tests.gpu_util import LSE_TOL, TOL, assert_close, device, max_abs, say, to_device, to_f64
+from tests.gpu_util import assert_close, device, max_abs, say, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +58,9 @@ CONTIGUOUS = [
     (2, 2, 128, 600, "f32", [600, 1], "bhnd"),
     (2, 2, 16, 90, "f32", [90, 45], "bnhd"),
     (2, 2, 32, 90, "f32", [3, 90], "bhnd"),
+    # more than 16 and more than 64 splits of 256 keys (the merge's later rounds)
+    (3, 2, 64, 20000, "bf16", [20000, 4200, 16385], "bhnd"),
+    (2, 1, 128, 17000, "f32", [17000, 5000], "bnhd"),
 ]
 
 
@@ -78,31 +81,36 @@ def test_decode_contiguous_parity(dev, B, H, d, n, dtype, lens, layout):
 
 
 PAGED = [
-    # (B, H, d, page_size, max_pages, dtype, lengths, spare pages)
-    (4, 2, 64, 16, 40, "bf16", [640, 1, 0, 333], 3),
-    (3, 4, 128, 32, 20, "bf16", [640, 257, 100], 0),
-    (3, 2, 64, 7, 100, "bf16", [700, 256, 13], 5),
-    (2, 2, 64, 300, 3, "f32", [900, 301], 1),
-    (3, 2, 32, 16, 20, "f32", [320, 17, 0], 2),
+    # (B, H, d, page_size, max_pages, dtype, lengths, spare pages, page layout)
+    (4, 2, 64, 16, 40, "bf16", [640, 1, 0, 333], 3, "nhd"),
+    (4, 2, 64, 16, 40, "bf16", [640, 1, 0, 333], 3, "hnd"),
+    (3, 4, 128, 32, 20, "bf16", [640, 257, 100], 0, "nhd"),
+    (3, 2, 64, 7, 100, "bf16", [700, 256, 13], 5, "hnd"),
+    (2, 2, 64, 300, 3, "f32", [900, 301], 1, "nhd"),
+    (3, 2, 32, 16, 20, "f32", [320, 17, 0], 2, "hnd"),
 ]
 
 
-def _paged(q, k, v, lens, page_size, max_pages, spare, seed, dev):
+def _paged(q, k, v, lens, page_size, max_pages, spare, seed, dev, layout="nhd"):
+    """Pools as (pages, slots, H, d) views: "nhd" storage as is, "hnd" storage
+    (pages, H, slots, d) through a transposed view."""
     import torch
     table, num_pages = workloads.page_table(lens, page_size, max_pages, seed=seed, spare=spare)
-    kp = to_device(workloads.paged_pool(k, table, lens, page_size, num_pages), dev)
-    vp = to_device(workloads.paged_pool(v, table, lens, page_size, num_pages), dev)
+    kp = to_device(workloads.paged_pool(k, table, lens, page_size, num_pages, layout), dev)
+    vp = to_device(workloads.paged_pool(v, table, lens, page_size, num_pages, layout), dev)
+    if layout == "hnd":
+        kp, vp = kp.transpose(1, 2), vp.transpose(1, 2)
     return kp, vp, torch.from_numpy(table).to(dev), table
 
 
-@pytest.mark.parametrize("B,H,d,P,max_pages,dtype,lens,spare", PAGED)
-def test_decode_paged_parity(dev, B, H, d, P, max_pages, dtype, lens, spare):
+@pytest.mark.parametrize("B,H,d,P,max_pages,dtype,lens,spare,layout", PAGED)
+def test_decode_paged_parity(dev, B, H, d, P, max_pages, dtype, lens, spare, layout):
     import torch
     n = P * max_pages
     q, k, v = _inputs(B, H, d, n, dtype, seed=1000 + P + d)
-    kp, vp, table, _ = _paged(q, k, v, lens, P, max_pages, spare, seed=77 + P, dev=dev)
+    kp, vp, table, _ = _paged(q, k, v, lens, P, max_pages, spare, seed=77 + P, dev=dev, layout=layout)
     kv_len = torch.tensor(lens, dtype=torch.int32, device=dev)
-    say(f"decode paged B={B} H={H} d={d} page={P} pages={max_pages} {dtype} lens={lens}")
+    say(f"decode paged {layout} B={B} H={H} d={d} page={P} pages={max_pages} {dtype} lens={lens}")
     o, lse = mha.attention_decode(to_device(q, dev), kp, vp, kv_len, block_table=table, return_lse=True)
     torch.cuda.synchronize()
     _check(o, lse, q, k, v, lens, dtype, "decode paged")
@@ -201,10 +209,36 @@ def test_decode_workload_parity(dev):
     x = workloads.make_inputs(w)
     lens = w.kv_lengths()
     table_np, num_pages = w.pages()
-    kp = to_device(workloads.paged_pool(x["k"], table_np, lens, w.page_size, num_pages), dev)
-    vp = to_device(workloads.paged_pool(x["v"], table_np, lens, w.page_size, num_pages), dev)
+    kp = to_device(workloads.paged_pool(x["k"], table_np, lens, w.page_size, num_pages, "hnd"), dev).transpose(1, 2)
+    vp = to_device(workloads.paged_pool(x["v"], table_np, lens, w.page_size, num_pages, "hnd"), dev).transpose(1, 2)
     say(f"decode workload {w.name}")
     o, lse = mha.attention_decode(to_device(x["q"], dev), kp, vp, torch.from_numpy(lens).to(dev),
                                   block_table=torch.from_numpy(table_np).to(dev), return_lse=True)
     torch.cuda.synchronize()
     _check(o, lse, x["q"], x["k"], x["v"], lens, w.dtype, "decode workload")
+
+
+def _first(t, B):
+    """The first B batch items of a stored tensor."""
+    return workloads.Stored(t.value[:B], t.dtype, t.raw[:B])
+
+
+def test_decode_workspace_reuse(dev):
+    """One workspace serves many calls in a row with changing lengths and
+    shapes (its contents from one call never leak into the next)."""
+    import torch
+    B, H, d, n = 4, 3, 64, 3000
+    q, k, v = _inputs(B, H, d, n, "bf16", seed=1600)
+    qd, kc, vc = to_device(q, dev), to_device(k, dev).transpose(1, 2), to_device(v, dev).transpose(1, 2)
+    ws = torch.full((mha.attention_decode_workspace_size(B, H, d, n),), 0x7F, dtype=torch.uint8, device=dev)
+    for i, lens in enumerate(([3000, 257, 1, 700], [2999, 2048, 0, 256], [513, 3000, 3000, 12], [1, 1, 1, 1])):
+        say(f"decode workspace reuse, call {i}: lens={lens}")
+        kv_len = torch.tensor(lens, dtype=torch.int32, device=dev)
+        o, lse = mha.attention_decode(qd, kc, vc, kv_len, workspace=ws, return_lse=True)
+        torch.cuda.synchronize()
+        _check(o, lse, q, k, v, lens, "bf16", f"workspace reuse call {i}")
+    # a smaller problem on the same (larger) workspace
+    kv_len = torch.tensor([600, 40], dtype=torch.int32, device=dev)
+    o, lse = mha.attention_decode(qd[:2].contiguous(), kc[:2], vc[:2], kv_len, workspace=ws, return_lse=True)
+    torch.cuda.synchronize()
+    _check(o, lse, _first(q, 2), _first(k, 2), _first(v, 2), [600, 40], "bf16", "smaller call")

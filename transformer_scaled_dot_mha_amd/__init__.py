@@ -52,6 +52,28 @@ def _stream_handle(dev, stream):
     return s.cuda_stream
 
 
+class _on_device:
+    """Make `dev` the current device for a library call; free when it already is
+    (the usual case), since a device switch costs more than the call itself."""
+    __slots__ = ("dev", "prev")
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.prev = None
+
+    def __enter__(self):
+        torch = _torch()
+        cur = torch.cuda.current_device()
+        if cur != self.dev.index:
+            self.prev = cur
+            torch.cuda.set_device(self.dev)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            _torch().cuda.set_device(self.prev)
+        return False
+
+
 def _kv_len_arg(kv_len, B, dev):
     """Check a key-length tensor: int32, on the device, (B,) contiguous."""
     torch = _torch()
@@ -94,7 +116,7 @@ def attention_forward(q, k, v, *, causal: bool = False, scale: float | None = No
     if scale is None:
         scale = 1.0 / math.sqrt(d_k)
     lib = load()
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, n_q, n_k, d_k, d_v,
                 strides3(q.stride()[:3]), strides3(k.stride()[:3]), strides3(v.stride()[:3]),
                 strides3(out.stride()[:3]), _dtype_code(q), int(bool(causal)), float(scale))
@@ -124,7 +146,7 @@ def linear_forward(x, w, *, out=None, stream=None):
     if tuple(out.shape) != (m, n) or out.stride(1) != 1:
         raise ValueError("out must be (m, n) row-major")
     lib = load()
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib.linear_forward(x.data_ptr(), w.data_ptr(), out.data_ptr(), m, n, k, x.stride(0),
                                 w.stride(0), out.stride(0), _dtype_code(x), _stream_handle(dev, stream))
     check(st)
@@ -168,7 +190,7 @@ def mha_forward(xq, xk, xv, wq, wk, wv, wo, heads: int, *, causal: bool = False,
         out = torch.empty((B, n_q, d_model), dtype=xq.dtype, device=dev)
     if tuple(out.shape) != (B, n_q, d_model) or not out.is_contiguous():
         raise ValueError("out must be a contiguous (B, N_q, d_model) tensor")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         args = (xq.data_ptr(), xk.data_ptr(), xv.data_ptr(), wq.data_ptr(), wk.data_ptr(),
                 wv.data_ptr(), wo.data_ptr(), out.data_ptr(), workspace.data_ptr(),
                 workspace.numel() * workspace.element_size(), B, n_q, n_k, d_model, heads,
@@ -223,7 +245,7 @@ def encoder_layer_forward(x, weights: dict, heads: int, *, eps: float = 1e-5, ca
         raise ValueError("out must be a contiguous (B, N, d_model) tensor of x's dtype")
     w = EncoderWeights(*[t.data_ptr() for t in ts])
     kvp = None if kv_len is None else _kv_len_arg(kv_len, B, dev)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib.encoder_layer_forward(x.data_ptr(), ctypes.byref(w), out.data_ptr(), workspace.data_ptr(),
                                        workspace.numel() * workspace.element_size(), B, N, d_model, heads, d_ff,
                                        float(eps), code, int(bool(causal)), kvp, _stream_handle(dev, stream))
@@ -250,6 +272,9 @@ def attention_decode(q, k_cache, v_cache, kv_len, *, block_table=None, scale: fl
         is in page block_table[b, j // slots] at slot j % slots.
     kv_len: int32 device tensor (B,). Returns out (B, H, d), and the fp32
     log-sum-exp (B, H) when return_lse is set.
+    workspace: optional uint8 device tensor of attention_decode_workspace_size
+    bytes (scratch; one call at a time per workspace), allocated per call if
+    omitted.
     """
     torch = _torch()
     dev = _require_device(q, k_cache, v_cache)
@@ -286,12 +311,13 @@ def attention_decode(q, k_cache, v_cache, kv_len, *, block_table=None, scale: fl
         raise ValueError("out must be a contiguous (B, H, d) tensor")
     lse = torch.empty((B, H), dtype=torch.float32, device=dev) if return_lse else None
     lib = load()
-    need = int(lib.attention_decode_workspace_size(B, H, d, max_len))
-    if workspace is None:
+    if workspace is None:   # the library checks a caller's workspace size itself
+        need = int(lib.attention_decode_workspace_size(B, H, d, max_len))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    cache = KVCache(k_cache.data_ptr(), v_cache.data_ptr(), table_p, k_cache.stride(0), k_cache.stride(1),
-                    k_cache.stride(2), page_size, max_pages, num_pages, max_len)
-    with torch.cuda.device(dev):
+    ks = k_cache.stride()
+    cache = KVCache(k_cache.data_ptr(), v_cache.data_ptr(), table_p, ks[0], ks[1], ks[2], page_size, max_pages,
+                    num_pages, max_len)
+    with _on_device(dev):
         st = lib.attention_decode(q.data_ptr(), ctypes.byref(cache), _kv_len_arg(kv_len, B, dev), out.data_ptr(),
                                   lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
                                   workspace.numel() * workspace.element_size(), B, H, d, _dtype_code(q),

@@ -18,8 +18,12 @@
 // coalesced 16-byte loads and many loads in flight, on the vector ALUs.
 //
 // Split over keys. Workgroup (bh, s) takes keys [256 s, 256 s + 256) of one
-// (batch, head); a later merge kernel combines the splits' partial softmax
-// states. Inside a workgroup each wavefront owns 64 keys; a key's d elements
+// (batch, head) and writes its partial softmax state (max, sum, unnormalised
+// output) to the workspace; a second, small launch merges the splits of each
+// (batch, head). A sequence of one split, or of none, is finished by the split
+// kernel itself. (Merging in the split kernel, by the last split to finish,
+// needs a release fence per workgroup, which on this chip writes back the
+// whole L2 and costs far more than the second launch.) Inside a workgroup each wavefront owns 64 keys; a key's d elements
 // are spread over d / 8 (bf16) or d / 4 (fp32) lanes, one 16-byte load each,
 // so one load instruction of a wavefront reads several whole key rows. Each
 // lane group keeps its own running max, sum and output slice (online softmax
@@ -106,6 +110,98 @@ __device__ __forceinline__ float to_elem<float>(float x) {
   return x;
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int x = 32; x > 0; x >>= 1) v = fmaxf(v, __shfl_xor(v, x, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int x = 32; x > 0; x >>= 1) v += __shfl_xor(v, x, 64);
+  return v;
+}
+
+// One wavefront combines the ns >= 2 split states of (batch, head) bh,
+// normalises and writes o and lse. The loads are issued together so the
+// wavefront waits for memory about twice (the length, then the rest): the split states one per lane and the
+// first kRows split output rows up front; splits past 64 or kRows (caches
+// longer than 16384 or 4096 keys) take further rounds.
+template <typename T, int D>
+__device__ void merge_splits(const DecodeArgs& a, int bh, int ns, int lane) {
+  constexpr int kE = (D + 63) / 64;  // output elements per lane
+  constexpr int kRows = 16;          // split rows loaded up front
+  const float* ml = a.part_ml + (int64_t)bh * a.splits * 2;
+  const float* po = a.part_o + (int64_t)bh * a.splits * D;
+
+  float pre[kRows][kE];
+#pragma unroll
+  for (int j = 0; j < kRows; ++j) {
+#pragma unroll
+    for (int e = 0; e < kE; ++e)
+      pre[j][e] = (j < ns && lane + 64 * e < D) ? po[(int64_t)j * D + lane + 64 * e] : 0.f;
+  }
+  float m0 = -INFINITY, l0 = 0.f;  // this lane's split of the first 64
+  if (lane < ns) {
+    m0 = ml[2 * lane];
+    l0 = ml[2 * lane + 1];
+  }
+  float mx = m0;
+  bool nan = m0 != m0;
+  for (int s = 64 + lane; s < ns; s += 64) {
+    const float ms = ml[2 * s];
+    nan |= ms != ms;
+    mx = fmaxf(mx, ms);
+  }
+  mx = wave_max(mx);
+  nan = __any(nan);
+
+  float lsum = 0.f;
+  float acc[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+  if (!nan) {
+    const float f0 = lane < ns ? exp2_fast(m0 - mx) : 0.f;
+    lsum = f0 * l0;
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      const float fj = __shfl(f0, j, 64);  // 0 for j >= ns
+#pragma unroll
+      for (int e = 0; e < kE; ++e) acc[e] += fj * pre[j][e];
+    }
+    // splits kRows.. (rare: caches longer than kRows * kChunk keys)
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      const int s = s0 + lane;
+      float f = s0 == 0 ? f0 : 0.f;
+      if (s0 > 0 && s < ns) {
+        f = exp2_fast(ml[2 * s] - mx);
+        lsum += f * ml[2 * s + 1];
+      }
+      const int first = s0 == 0 ? kRows : 0;
+      const int cnt = min(64, ns - s0);
+      for (int j = first; j < cnt; ++j) {
+        const float fj = __shfl(f, j, 64);
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+          if (lane + 64 * e < D) acc[e] += fj * po[(int64_t)(s0 + j) * D + lane + 64 * e];
+      }
+    }
+    lsum = wave_sum(lsum);
+  }
+  float scale_out, lse;
+  if (nan) {
+    scale_out = NAN;
+    lse = NAN;
+  } else {
+    scale_out = 1.0f / lsum;
+    lse = (mx + __log2f(lsum)) * kLn2;
+  }
+  T* out = static_cast<T*>(a.o) + (int64_t)bh * D;
+#pragma unroll
+  for (int e = 0; e < kE; ++e)
+    if (lane + 64 * e < D) out[lane + 64 * e] = to_elem<T>(nan ? NAN : acc[e] * scale_out);
+  if (a.lse != nullptr && lane == 0) a.lse[bh] = lse;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   typedef Vec16<T> V;
@@ -128,9 +224,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int h = bh - b * a.heads;
   const int len = min(max(a.kv_len[b], 0), a.max_len);
   const int key0 = split * kChunk;
-  if (key0 >= len) return;  // uniform over the workgroup, before any barrier
-
   const int tid = threadIdx.x;
+  if (key0 >= len) {  // uniform over the workgroup, before any barrier
+    if (len == 0 && split == 0) {  // an empty cache: no softmax, o = 0 and lse = -inf
+      if (tid < D) static_cast<T*>(a.o)[(int64_t)bh * D + tid] = to_elem<T>(0.f);
+      if (a.lse != nullptr && tid == 0) a.lse[bh] = -INFINITY;
+    }
+    return;
+  }
+
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
@@ -138,8 +240,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // Keys past len reuse the chunk's first row, which is valid; their scores
   // are masked below.
   int bad = 0;
-  {
-    const int j = key0 + tid < len ? key0 + tid : key0;
+#pragma unroll
+  for (int t = tid; t < kChunk; t += 256) {
+    const int j = key0 + t < len ? key0 + t : key0;
     int64_t off;
     if (a.block_table != nullptr) {
       int page = a.block_table[(int64_t)b * a.max_pages + j / a.page_size];
@@ -151,7 +254,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     } else {
       off = (int64_t)b * a.page_stride + (int64_t)j * a.row_stride;
     }
-    s_off[tid] = off;
+    s_off[t] = off;
   }
   const int any_bad = __syncthreads_or(bad);
 
@@ -178,11 +281,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int it = 0; it < kIters; ++it) {
       const int ib = wave * kKeysPerWave + it * kKpi;  // chunk-local first key
       if (key0 + ib >= len) break;                     // uniform over the wavefront
+      // each cached row is read once per step: nontemporal loads keep it from
+      // displacing reusable lines in the caches
       typename V::raw kr[kU], vr[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) kr[u] = *reinterpret_cast<const typename V::raw*>(kb + s_off[ib + u * kKpl + g]);
+      for (int u = 0; u < kU; ++u)
+        kr[u] = __builtin_nontemporal_load(reinterpret_cast<const typename V::raw*>(kb + s_off[ib + u * kKpl + g]));
 #pragma unroll
-      for (int u = 0; u < kU; ++u) vr[u] = *reinterpret_cast<const typename V::raw*>(vb + s_off[ib + u * kKpl + g]);
+      for (int u = 0; u < kU; ++u)
+        vr[u] = __builtin_nontemporal_load(reinterpret_cast<const typename V::raw*>(vb + s_off[ib + u * kKpl + g]));
 
       float s[kU];
 #pragma unroll
@@ -243,7 +350,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // wavefronts -> the split's partial state
+  // wavefronts -> the split's state; a sequence of one split is final here
+  const int ns = (len + kChunk - 1) / kChunk;
   if (tid < D) {
     float mw = -INFINITY;
 #pragma unroll
@@ -256,64 +364,31 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       lw += s_l[w] * f;
       ow += s_o[w][tid] * f;
     }
-    const int64_t part = (int64_t)bh * a.splits + split;
-    a.part_o[part * D + tid] = ow;
-    if (tid == 0) {
-      a.part_ml[2 * part] = any_bad ? NAN : mw;
-      a.part_ml[2 * part + 1] = any_bad ? NAN : lw;
+    if (ns == 1) {
+      static_cast<T*>(a.o)[(int64_t)bh * D + tid] = to_elem<T>(any_bad ? NAN : ow / lw);
+      if (a.lse != nullptr && tid == 0) a.lse[bh] = any_bad ? NAN : (mw + __log2f(lw)) * kLn2;
+    } else {
+      const int64_t part = (int64_t)bh * a.splits + split;
+      a.part_o[part * D + tid] = ow;
+      if (tid == 0) {
+        a.part_ml[2 * part] = any_bad ? NAN : mw;
+        a.part_ml[2 * part + 1] = any_bad ? NAN : lw;
+      }
     }
   }
 }
 
-// One wavefront per (batch, head): combine the splits, normalise, write o and lse.
+// One wavefront per (batch, head) of two or more splits (the others were
+// finished by the split kernel): merge_splits.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int kE = (D + 63) / 64;  // output elements per lane
   const int lane = threadIdx.x & 63;
   const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (bh >= a.batch * a.heads) return;  // uniform over the wavefront; no barrier follows
-  const int b = bh / a.heads;
-  const int len = min(max(a.kv_len[b], 0), a.max_len);
+  const int len = min(max(a.kv_len[bh / a.heads], 0), a.max_len);
   const int ns = (len + kChunk - 1) / kChunk;
-  const float* ml = a.part_ml + (int64_t)bh * a.splits * 2;
-  const float* po = a.part_o + (int64_t)bh * a.splits * D;
-
-  float mx = -INFINITY;
-  bool nan = false;
-  for (int s = 0; s < ns; ++s) {
-    const float ms = ml[2 * s];
-    nan |= ms != ms;
-    mx = fmaxf(mx, ms);
-  }
-  float lsum = 0.f;
-  float acc[kE];
-#pragma unroll
-  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
-  if (!nan) {
-    for (int s = 0; s < ns; ++s) {
-      const float f = exp2_fast(ml[2 * s] - mx);
-      lsum += f * ml[2 * s + 1];
-#pragma unroll
-      for (int e = 0; e < kE; ++e)
-        if (lane + 64 * e < D) acc[e] += f * po[(int64_t)s * D + lane + 64 * e];
-    }
-  }
-  float scale_out, lse;
-  if (ns == 0) {
-    scale_out = 0.f;
-    lse = -INFINITY;
-  } else if (nan) {
-    scale_out = NAN;
-    lse = NAN;
-  } else {
-    scale_out = 1.0f / lsum;
-    lse = (mx + __log2f(lsum)) * kLn2;
-  }
-  T* out = static_cast<T*>(a.o) + (int64_t)bh * D;
-#pragma unroll
-  for (int e = 0; e < kE; ++e)
-    if (lane + 64 * e < D) out[lane + 64 * e] = to_elem<T>(nan ? NAN : acc[e] * scale_out);
-  if (a.lse != nullptr && lane == 0) a.lse[bh] = lse;
+  if (ns < 2) return;
+  merge_splits<T, D>(a, bh, ns, lane);
 }
 
 template <typename T, int D>

@@ -57,7 +57,8 @@ struct AddNormArgs {
 
 // One decoding step: query (batch, heads, d) against the first kv_len[b] keys
 // and values of a cache (see decode.hip for the addressing). Strides in
-// elements. Partial softmax states of the key splits go to part_ml / part_o.
+// elements. Partial softmax states of the key splits go to part_ml / part_o
+// and a second launch merges them.
 constexpr int kDecodeChunk = 256;  // keys per split
 struct DecodeArgs {
   const void* q;  // (batch, heads, d) contiguous

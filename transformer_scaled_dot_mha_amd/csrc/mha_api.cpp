@@ -337,13 +337,18 @@ mha_status encoder_layer_impl(const void* x, const mha_encoder_weights* wts, voi
 
 // Decode workspace: per (batch, head, split) the running max and sum, then
 // the unnormalised output row, both fp32.
-bool decode_ws_layout(int batch, int heads, int d, int max_len, size_t* o_off, size_t* total) {
+struct DecodeWs {
+  size_t ml, o, total;
+};
+
+bool decode_ws_layout(int batch, int heads, int d, int max_len, DecodeWs* w) {
   const int64_t splits = ((int64_t)max_len + mha::kDecodeChunk - 1) / mha::kDecodeChunk;
   const unsigned __int128 parts = (unsigned __int128)batch * heads * splits;
   const unsigned __int128 tot = parts * (2 + d) * 4 + 2 * kAlign;
   if (tot > ((unsigned __int128)1 << 62)) return false;
-  *o_off = round_up((size_t)(parts * 2 * 4));
-  *total = *o_off + round_up((size_t)(parts * d * 4));
+  w->ml = 0;
+  w->o = round_up((size_t)(parts * 2 * 4));
+  w->total = w->o + round_up((size_t)(parts * d * 4));
   return true;
 }
 
@@ -385,11 +390,10 @@ mha_status decode_impl(const void* q, const mha_kv_cache* cache, const int32_t* 
   const int64_t splits = ((int64_t)cache->max_len + mha::kDecodeChunk - 1) / mha::kDecodeChunk;
   if (bhs > INT32_MAX || splits > 65535)
     return fail(MHA_ERR_UNSUPPORTED, "too many (batch, head) pairs or max_len too large for one launch");
-  size_t o_off = 0, total = 0;
-  if (!decode_ws_layout(batch, heads, d, cache->max_len, &o_off, &total))
-    return fail(MHA_ERR_INVALID_ARG, "sizes overflow");
-  if (workspace_bytes < total)
-    return fail(MHA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, total);
+  DecodeWs ws;
+  if (!decode_ws_layout(batch, heads, d, cache->max_len, &ws)) return fail(MHA_ERR_INVALID_ARG, "sizes overflow");
+  if (workspace_bytes < ws.total)
+    return fail(MHA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, ws.total);
 
   mha::DecodeArgs a = {};
   a.q = q;
@@ -406,8 +410,8 @@ mha_status decode_impl(const void* q, const mha_kv_cache* cache, const int32_t* 
   a.head_stride = cache->head_stride;
   a.o = o;
   a.lse = lse;
-  a.part_ml = static_cast<float*>(workspace);
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_off);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.o);
   a.batch = batch;
   a.heads = heads;
   a.d = d;
@@ -537,9 +541,9 @@ mha_status encoder_layer_forward(const void* x, const mha_encoder_weights* weigh
 
 size_t attention_decode_workspace_size(int batch, int heads, int d, int max_len) {
   if (batch < 1 || heads < 1 || d < 1 || max_len < 1) return 0;
-  size_t o_off = 0, total = 0;
-  if (!decode_ws_layout(batch, heads, d, max_len, &o_off, &total)) return 0;
-  return total;
+  DecodeWs ws;
+  if (!decode_ws_layout(batch, heads, d, max_len, &ws)) return 0;
+  return ws.total;
 }
 
 mha_status attention_decode(const void* q, const mha_kv_cache* cache, const int32_t* kv_len, void* o, float* lse,

@@ -128,7 +128,8 @@ WORKLOADS: dict[str, Workload] = {
         Workload("base_encoder_layer_bf16_b32_n512", "layer", "bf16", batch=32, heads=8,
                  n_q=512, n_k=512, d_k=64, causal=False, seed=7, d_model=512, d_ff=2048),
         # one decoding step of the base model (8 heads of 64) for 64 sequences against a
-        # paged K/V cache of 16-slot pages; cached lengths uniform in [1024, 4096]
+        # paged K/V cache of 16-slot pages, each page stored head-major (H, 16, d);
+        # cached lengths uniform in [1024, 4096]
         Workload("decode_paged_bf16_b64_h8_kv4096", "decode", "bf16", batch=64, heads=8,
                  n_q=1, n_k=4096, d_k=64, causal=False, seed=8, kv_len_range=(1024, 4096), page_size=16),
     ]
@@ -287,18 +288,24 @@ def page_table(lengths, page_size: int, max_pages: int, seed: int, spare: int = 
     return table, num_pages
 
 
-def paged_pool(stored: Stored, table, lengths, page_size: int, num_pages: int) -> Stored:
-    """Move a logical cache (B, H, N, d) into a page pool (num_pages, page_size,
-    H, d) laid out by `table` (rows only move; slots no sequence owns stay 0).
-    The returned Stored carries the raw pool only (value is None)."""
+def paged_pool(stored: Stored, table, lengths, page_size: int, num_pages: int, layout: str = "nhd") -> Stored:
+    """Move a logical cache (B, H, N, d) into a page pool laid out by `table`
+    (rows only move; slots no sequence owns stay 0): layout "nhd" gives
+    (num_pages, page_size, H, d), "hnd" gives (num_pages, H, page_size, d), where
+    each head's part of a page is one contiguous run. The returned Stored
+    carries the raw pool only (value is None)."""
     raw = stored.raw
     B, H, N, d = raw.shape
-    pool = np.zeros((num_pages, page_size, H, d), dtype=raw.dtype)
+    shape = (num_pages, page_size, H, d) if layout == "nhd" else (num_pages, H, page_size, d)
+    pool = np.zeros(shape, dtype=raw.dtype)
     for b in range(B):
         n_pages = (int(lengths[b]) + page_size - 1) // page_size
         for i in range(n_pages):
             rows = raw[b, :, i * page_size:(i + 1) * page_size, :]     # (H, <=page_size, d)
-            pool[table[b, i], :rows.shape[1]] = rows.transpose(1, 0, 2)
+            if layout == "nhd":
+                pool[table[b, i], :rows.shape[1]] = rows.transpose(1, 0, 2)
+            else:
+                pool[table[b, i], :, :rows.shape[1]] = rows
     return Stored(None, stored.dtype, pool)
 
 
