@@ -155,6 +155,62 @@ def attention_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool =
     return o, rowsum, lse
 
 
+def attention_backward_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, *, causal: bool = False,
+                           scale: float | None = None, kv_len=None):
+    """Gradients of the attention output with respect to Q, K and V.
+
+    The pages motivate the 1/sqrt(d_k) scale by the gradient that flows back
+    through the softmax: a saturated (nearly one-hot) row passes almost none
+    ("32 Transformer" (ml-canon-en.vercel.app), "Why we divide by sqrt(dk)";
+    "How Transformers Work" (worksonmygpu.com), "Scaled dot-product
+    attention", step 2; "The Transformer" (hoshank.vercel.app), "The
+    Breakthrough"). This is that backward pass, the chain rule written out for
+    a loss whose gradient with respect to O is `do`:
+
+      O = P V                    ->  dV = P^T dO,    dP = dO V^T
+      P_i = softmax(S_i), each row ->  dS_i = J_i dP_i with the softmax Jacobian
+                                     J_i = diag(P_i) - P_i P_i^T, that is
+                                     dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)
+      S = scale Q K^T (+ masks)  ->  dQ = scale dS K,  dK = scale dS^T Q
+
+    Masked scores are constants (-inf), so no gradient reaches them: their
+    weights are 0 and so is dS there. A row with no visible key has P = 0 and
+    passes nothing. q, k, do: as in attention_ref; returns (dQ, dK, dV) of the
+    shapes of q, k and v, in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, n_q, d_k = q.shape
+    n_k = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if causal and n_q != n_k:
+        raise ValueError("the causal mask is defined for N_q == N_k only")
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            s = np.matmul(q[b, h], k[b, h].T) * scale
+            if causal:
+                s = s + causal_mask(n_q)
+            if kv_len is not None:
+                s = s + key_padding_mask_row(n_k, min(max(int(kv_len[b]), 0), n_k))[None, :]
+            dead = np.all(s == -np.inf, axis=-1)
+            s = np.where(dead[:, None], 0.0, s)
+            e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+            p = e / np.sum(e, axis=-1, keepdims=True)
+            p[dead] = 0.0
+            dp = np.matmul(do[b, h], v[b, h].T)
+            ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+            dv[b, h] = np.matmul(p.T, do[b, h])
+            dq[b, h] = scale * np.matmul(ds, k[b, h])
+            dk[b, h] = scale * np.matmul(ds.T, q[b, h])
+    return dq, dk, dv
+
+
 def causal_mask_rows(n: int, rows) -> np.ndarray:
     """The rows `rows` of causal_mask(n), formed without the full n x n matrix."""
     rows = np.asarray(rows)

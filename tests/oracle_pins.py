@@ -614,6 +614,132 @@ def check_paged_gather(gather):
     assert gather(pool, order, P, 0).shape == (H, 0, d)
 
 
+# ------------------------------------------------------------------ backward pass
+def _loss_grad_fd(attn, q, k, v, do, causal, kv_len, h=1e-6):
+    """Central differences of L = sum(dO * O) with respect to every element of
+    q, k and v, through the (separately pinned) forward oracle."""
+    def loss(qq, kk, vv):
+        return float(np.sum(do * attn(qq, kk, vv, causal=causal, kv_len=kv_len)[0]))
+    grads = []
+    for which in range(3):
+        args = [q.copy(), k.copy(), v.copy()]
+        g = np.zeros_like(args[which])
+        for idx in np.ndindex(*g.shape):
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            g[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def check_backward_finite_differences(bwd, attn):
+    """The backward matches central differences of sum(dO * O) through the
+    forward, unmasked (N_q != N_k), causal, and with key padding (incl. 0)."""
+    r = _rng(70)
+    cases = [(dict(causal=False, kv_len=None), (1, 2, 3, 4, 3)),
+             (dict(causal=True, kv_len=None), (1, 1, 5, 5, 3)),
+             (dict(causal=False, kv_len=[2, 0, 4]), (3, 1, 3, 4, 2)),
+             (dict(causal=True, kv_len=[3, 5]), (2, 1, 5, 5, 2))]
+    for kw, (B, H, nq, nk, d) in cases:
+        q, k, v = r.standard_normal((B, H, nq, d)), r.standard_normal((B, H, nk, d)), r.standard_normal((B, H, nk, d))
+        do = r.standard_normal((B, H, nq, d))
+        want = _loss_grad_fd(attn, q, k, v, do, kw["causal"], kw["kv_len"])
+        got = bwd(q, k, v, do, **kw)
+        for name, g, w in zip(("dQ", "dK", "dV"), got, want):
+            assert np.allclose(g, w, rtol=0, atol=1e-7), f"{name} vs finite differences ({kw})"
+
+
+def check_backward_torch(bwd):
+    """Cross-check: torch float64 autograd through scaled_dot_product_attention
+    (CPU), unmasked, causal, and with a boolean key mask (True = may attend)."""
+    import torch
+    import torch.nn.functional as F
+    r = _rng(71)
+    B, H, n, d = 2, 3, 9, 4
+    q, k, v = r.standard_normal((B, H, n, d)), r.standard_normal((B, H, n, d)), r.standard_normal((B, H, n, d))
+    do = r.standard_normal((B, H, n, d))
+    lens = [9, 4]
+    for causal, kv_len in ((False, None), (True, None), (False, lens), (True, lens)):
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        mask = None
+        if kv_len is not None:
+            mask = torch.zeros(B, 1, n, n, dtype=torch.bool)
+            for b, L in enumerate(kv_len):
+                mask[b, :, :, :L] = True
+            if causal:
+                mask &= torch.ones(n, n, dtype=torch.bool).tril()
+        o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, is_causal=causal and mask is None)
+        o.backward(torch.tensor(do))
+        got = bwd(q, k, v, do, causal=causal, kv_len=kv_len)
+        for name, g, t in zip(("dQ", "dK", "dV"), got, (tq, tk, tv)):
+            assert np.allclose(g, t.grad.numpy(), rtol=0, atol=1e-12), f"{name} vs torch ({causal}, {kv_len})"
+
+
+def check_backward_invariants(bwd):
+    """Facts that hold for any inputs: every softmax Jacobian row sums to 0, so
+    the key gradients sum to 0 over the keys; the weights sum to 1, so the value
+    gradients sum to the sum of dO; with one key nothing reaches Q or K; the
+    backward is linear in dO; under the causal mask the gradients of keys j and
+    later do not depend on earlier queries; padded keys get exactly 0 and the
+    rest equal the gradient of the truncated problem."""
+    q, k, v = _qkv(72, B=2, H=2, nq=6, nk=6, d=4)
+    do = _rng(73).standard_normal(q.shape)
+    dq, dk, dv = bwd(q, k, v, do)
+    assert np.allclose(dk.sum(axis=2), 0.0, atol=1e-12), "key gradients must sum to 0"
+    assert np.allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12), "value gradients must sum to sum(dO)"
+    dq1, dk1, dv1 = bwd(q, k[:, :, :1], v[:, :, :1], do)
+    assert np.all(np.abs(dq1) < 1e-14) and np.all(np.abs(dk1) < 1e-14), "one key: no gradient to Q or K"
+    assert np.allclose(dv1[:, :, 0], do.sum(axis=2), atol=1e-12)
+    do2 = _rng(74).standard_normal(q.shape)
+    lin = bwd(q, k, v, do + 2.0 * do2)
+    for a, b_, c in zip(lin, (dq, dk, dv), bwd(q, k, v, do2)):
+        assert np.allclose(a, b_ + 2.0 * c, atol=1e-12), "linear in dO"
+    # causal locality: change queries and dO before position j0
+    j0 = 3
+    base = bwd(q, k, v, do, causal=True)
+    q2, do3 = q.copy(), do.copy()
+    q2[:, :, :j0] += 5.0
+    do3[:, :, :j0] -= 2.0
+    moved = bwd(q2, k, v, do3, causal=True)
+    assert np.allclose(moved[1][:, :, j0:], base[1][:, :, j0:], atol=1e-13), "causal dK locality"
+    assert np.allclose(moved[2][:, :, j0:], base[2][:, :, j0:], atol=1e-13), "causal dV locality"
+    # padding
+    L = 4
+    pq, pk, pv = bwd(q, k, v, do, kv_len=[L, L])
+    tq, tk, tv = bwd(q, k[:, :, :L], v[:, :, :L], do)
+    assert np.all(pk[:, :, L:] == 0.0) and np.all(pv[:, :, L:] == 0.0), "padded keys get no gradient"
+    assert np.allclose(pq, tq, atol=1e-13) and np.allclose(pk[:, :, :L], tk, atol=1e-13)
+    assert np.allclose(pv[:, :, :L], tv, atol=1e-13)
+    zq, zk, zv = bwd(q, k, v, do, kv_len=[0, 6])
+    assert np.all(zq[0] == 0.0) and np.all(zk[0] == 0.0) and np.all(zv[0] == 0.0), "no visible key: no gradient"
+
+
+def check_backward_saturation(bwd):
+    """The pages' reason for the scale: large logits saturate the softmax
+    (nearly one-hot rows) and then almost no gradient passes through it. With
+    K = I and each query t times a distinct basis vector, row i's scores are
+    scale * t at one key and 0 elsewhere: at t = 1 the gradients to Q and K are
+    live; at t = 200 the rows are one-hot to within exp(-70), dQ and dK vanish,
+    and dV only routes each dO row to its query's key."""
+    d = 8
+    perm = np.array([3, 0, 7, 1, 6, 2, 5, 4])
+    k = np.eye(d)[None, None]
+    v = _rng(75).standard_normal((1, 1, d, d))
+    do = _rng(76).standard_normal((1, 1, d, d))
+    grads = {}
+    for t in (1.0, 200.0):
+        q = (t * np.eye(d)[perm])[None, None]
+        grads[t] = bwd(q, k, v, do)
+    live, frozen = grads[1.0], grads[200.0]
+    assert np.linalg.norm(live[0]) > 0.05 * np.linalg.norm(do), "gradients to Q live at t = 1"
+    assert np.linalg.norm(frozen[0]) < 1e-12 * np.linalg.norm(live[0]), "dQ must vanish at saturation"
+    assert np.linalg.norm(frozen[1]) < 1e-12 * np.linalg.norm(live[1]), "dK must vanish at saturation"
+    routed = np.zeros((d, d))
+    routed[perm] = do[0, 0]                 # key perm[i] receives query i's dO row
+    assert np.allclose(frozen[2][0, 0], routed, atol=1e-12), "dV routes dO rows through the one-hot weights"
+
 ATTENTION_PINS = [check_rows_sum_to_one, check_permutation_equivariance,
                   check_constant_v_and_convex_hull, check_causal_locality,
                   check_masked_weight_is_zero, check_closed_forms, check_low_temperature_argmax,

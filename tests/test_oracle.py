@@ -112,3 +112,19 @@ def test_decode_is_last_causal_row():
 
 def test_paged_gather():
     pins.check_paged_gather(oracle.gather_pages)
+
+
+def test_backward_finite_differences():
+    pins.check_backward_finite_differences(oracle.attention_backward_ref, oracle.attention_ref)
+
+
+def test_backward_torch():
+    pins.check_backward_torch(oracle.attention_backward_ref)
+
+
+def test_backward_invariants():
+    pins.check_backward_invariants(oracle.attention_backward_ref)
+
+
+def test_backward_saturation():
+    pins.check_backward_saturation(oracle.attention_backward_ref)

@@ -257,3 +257,65 @@ def test_unmutated_decode_passes():
     decode, gather = _mutant_decode("none")
     pins.check_decode_is_last_causal_row(decode, oracle.attention_ref)
     pins.check_paged_gather(gather)
+
+
+def _mutant_backward(mutation):
+    """The attention backward with one planted mistake."""
+    def bwd(q, k, v, do, *, causal=False, scale=None, kv_len=None):
+        q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+        B, H, nq, d = q.shape
+        nk = k.shape[2]
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(B):
+            for h in range(H):
+                s = q[b, h] @ k[b, h].T * scale
+                if causal and mutation != "causal_dropped":
+                    s = np.where(np.arange(nk)[None, :] > np.arange(nq)[:, None], -np.inf, s)
+                if kv_len is not None and mutation != "padding_dropped":
+                    L = min(max(int(kv_len[b]), 0), nk)
+                    s = np.where(np.arange(nk)[None, :] >= L, -np.inf, s)
+                dead = np.all(s == -np.inf, axis=-1)
+                s = np.where(dead[:, None], 0.0, s)
+                e = np.exp(s - s.max(-1, keepdims=True))
+                p = e / e.sum(-1, keepdims=True)
+                p[dead] = 0.0
+                vv = k[b, h] if mutation == "dp_uses_k" else v[b, h]
+                dp = do[b, h] @ vv.T
+                if mutation == "no_row_term":
+                    ds = p * dp
+                elif mutation == "row_term_wrong_axis":
+                    ds = p * (dp - np.sum(p * dp, axis=0, keepdims=True))
+                else:
+                    ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+                if mutation == "ds_sign_flip":
+                    ds = -ds
+                dv[b, h] = (p @ do[b, h]) if mutation == "dv_not_transposed" else p.T @ do[b, h]
+                dq[b, h] = (1.0 if mutation == "dq_scale_dropped" else scale) * (ds @ k[b, h])
+                sk = scale * scale if mutation == "dk_scale_twice" else scale
+                dk[b, h] = sk * ((ds @ q[b, h]) if mutation == "dk_not_transposed" else ds.T @ q[b, h])
+        return dq, dk, dv
+    return bwd
+
+
+BACKWARD_MUTANTS = ["dq_scale_dropped", "dk_scale_twice", "no_row_term", "row_term_wrong_axis", "ds_sign_flip",
+                    "dv_not_transposed", "dk_not_transposed", "dp_uses_k", "causal_dropped", "padding_dropped"]
+
+
+@pytest.mark.parametrize("mutation", BACKWARD_MUTANTS)
+def test_backward_mutant_is_caught(mutation):
+    bwd = _mutant_backward(mutation)
+    checks = [lambda: pins.check_backward_finite_differences(bwd, oracle.attention_ref),
+              lambda: pins.check_backward_torch(bwd),
+              lambda: pins.check_backward_invariants(bwd),
+              lambda: pins.check_backward_saturation(bwd)]
+    assert any(_caught(c) for c in checks), f"no pin catches the mutant {mutation!r}"
+
+
+def test_unmutated_backward_passes():
+    bwd = _mutant_backward("none")
+    pins.check_backward_finite_differences(bwd, oracle.attention_ref)
+    pins.check_backward_torch(bwd)
+    pins.check_backward_invariants(bwd)
+    pins.check_backward_saturation(bwd)
