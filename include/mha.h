@@ -83,6 +83,7 @@ typedef enum mha_dtype { MHA_F32 = 0, MHA_BF16 = 1 } mha_dtype;
  *   MHA_ERR_UNSUPPORTED.
  * Alignment: base pointers 16-byte aligned; every stride a multiple of
  *   8 elements (bf16) or 4 elements (f32). Otherwise MHA_ERR_INVALID_ARG.
+ *   Row strides above 2^24 elements are MHA_ERR_UNSUPPORTED.
  */
 mha_status attention_forward(const void* q, const void* k, const void* v, void* o,
                              int batch, int heads, int n_q, int n_k, int d_k, int d_v,
@@ -234,6 +235,53 @@ mha_status encoder_layer_forward(const void* x, const mha_encoder_weights* weigh
                                  void* workspace, size_t workspace_bytes, int batch, int n, int d_model,
                                  int heads, int d_ff, float eps, mha_dtype dtype, int causal,
                                  const int32_t* kv_len, void* stream);
+
+/*
+ * attention_backward -- gradients of attention_forward with respect to Q, K
+ * and V, given the gradient dO of a loss with respect to the output:
+ *   dV = P^T dO,   dP = dO V^T,   dS_ij = P_ij (dP_ij - delta_i),
+ *   delta_i = sum_j P_ij dP_ij = dO_i . O_i,
+ *   dQ = scale dS K,   dK = scale dS^T Q,
+ * the chain rule through O = P V, the row softmax (Jacobian
+ * diag(P_i) - P_i P_i^T) and S = scale Q K^T. Masked scores are constants, so
+ * masked pairs pass no gradient. The pages give this gradient as the reason
+ * for the 1/sqrt(d_k) scale: a saturated softmax passes almost none ("32
+ * Transformer" (ml-canon-en.vercel.app), "Why we divide by sqrt(dk)"; "How
+ * Transformers Work" (worksonmygpu.com), "Scaled dot-product attention",
+ * step 2; "The Transformer" (hoshank.vercel.app), "The Breakthrough").
+ *
+ * q, k, v, o, d_o: as attention_forward's q, k, v, o (o is the forward's
+ *   output for these inputs, d_o has o's shape); dq, dk, dv: outputs of the
+ *   shapes of q, k, v. Each tensor has its own {batch, head, row} element
+ *   strides; last dimension contiguous. All device memory, of `dtype`.
+ * lse: DEVICE fp32 (batch, heads, n_q), 16-byte aligned: the log-sum-exp that
+ *   attention_forward / attention_forward_padded returned for the same q, k,
+ *   scale, causal flag and kv_len. P is recomputed from it exactly
+ *   (P_ij = exp(scale q_i.k_j - lse_i)); an lse that does not belong to these
+ *   inputs gives meaningless gradients (not detected). -inf marks a row with
+ *   no visible key: it passes no gradient.
+ * causal, scale, kv_len: as in attention_forward_padded (kv_len may be NULL).
+ *   Keys at or past kv_len[b] get dK = dV = 0.
+ * workspace: DEVICE scratch of at least attention_backward_workspace_size()
+ *   bytes (delta, fp32 per query row), 16-byte aligned.
+ * Supported: as attention_forward (bf16: d = 64; f32: d in {16, 32, 64, 128}).
+ * bf16: P and dS are rounded to bf16 for the matrix products (as P is in the
+ *   forward), every accumulation is fp32, and dq, dk, dv are rounded once.
+ * Launches, both on `stream`: dQ with delta (a workgroup per query block),
+ *   then dK and dV (a workgroup per key block); no atomics, so the result is
+ *   deterministic.
+ * Outputs must not overlap any input.
+ */
+size_t attention_backward_workspace_size(int batch, int heads, int n_q);
+
+mha_status attention_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                              const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int n_q,
+                              int n_k, int d, const int64_t q_strides[3], const int64_t k_strides[3],
+                              const int64_t v_strides[3], const int64_t o_strides[3],
+                              const int64_t do_strides[3], const int64_t dq_strides[3],
+                              const int64_t dk_strides[3], const int64_t dv_strides[3], mha_dtype dtype,
+                              int causal, float scale, const int32_t* kv_len, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * attention_decode -- one decoding step against a key/value cache: for every

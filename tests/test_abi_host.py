@@ -37,6 +37,7 @@ def test_header_declares_the_boundary():
     assert {"attention_forward", "attention_forward_padded", "mha_forward", "mha_forward_padded",
             "mha_forward_workspace_size", "linear_forward", "encoder_layer_workspace_size",
             "encoder_layer_forward", "attention_decode_workspace_size", "attention_decode",
+            "attention_backward_workspace_size", "attention_backward",
             "mha_status_string", "mha_last_error", "mha_version"} == set(fns)
     assert set(fns) == set(_lib.SIGNATURES), "binding signatures out of sync with include/mha.h"
 
@@ -289,3 +290,36 @@ def test_decode_workspace_size(lib):
         parts = B * H * ((n + 255) // 256)
         assert lib.attention_decode_workspace_size(B, H, d, n) == r(parts * 8) + r(parts * d * 4)
     assert lib.attention_decode_workspace_size(1, 1, 64, 0) == 0
+
+
+def bwd(lib, q=FAKE, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 30, B=2, H=8, nq=64, nk=64, d=64, strides=None,
+        dtype=_lib.MHA_BF16, causal=0, scale=0.125, kv_len=None):
+    st = [S_BHND] * 8 if strides is None else strides
+    return lib.attention_backward(q, FAKE, FAKE, FAKE, FAKE, lse, dq, FAKE, FAKE, B, H, nq, nk, d,
+                                  *[_lib.strides3(x) for x in st], dtype, causal, scale, kv_len, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(lse=None), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(dq=None), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(ws=None), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(dq=MIS), _lib.MHA_ERR_INVALID_ARG, "aligned"),
+    (dict(lse=FAKE + 4), _lib.MHA_ERR_INVALID_ARG, "aligned"),
+    (dict(d=32), _lib.MHA_ERR_UNSUPPORTED, "d_k = 64"),
+    (dict(causal=1, nk=65), _lib.MHA_ERR_INVALID_ARG, "causal"),
+    (dict(ws_bytes=100), _lib.MHA_ERR_WORKSPACE, "required"),
+    (dict(kv_len=FAKE + 2), _lib.MHA_ERR_INVALID_ARG, "kv_len"),
+    (dict(strides=[S_BHND] * 5 + [(8 * 64 * 64, 64 * 64, 12)] + [S_BHND] * 2), _lib.MHA_ERR_INVALID_ARG, "dq stride"),
+    (dict(strides=[(8 * 64 * 64, 64 * 64, 1 << 25)] + [S_BHND] * 7), _lib.MHA_ERR_UNSUPPORTED, "row stride"),
+    (dict(strides=[S_BHND] * 4 + [(8 * 64 * 64, 64 * 64, 1 << 25)] + [S_BHND] * 3), _lib.MHA_ERR_UNSUPPORTED,
+     "d_o row stride"),
+])
+def test_backward_validation(lib, kw, status, needle):
+    assert bwd(lib, **kw) == status
+    assert needle in lib.mha_last_error().decode()
+
+
+def test_backward_workspace_size(lib):
+    assert lib.attention_backward_workspace_size(2, 8, 100) == (2 * 8 * 100 * 4 + 255) // 256 * 256
+    assert lib.attention_backward_workspace_size(0, 8, 100) == 0

@@ -15,7 +15,8 @@ from ._lib import (ENCODER_WEIGHT_NAMES, EncoderWeights, KVCache, MHA_BF16, MHA_
                    MHA_ERR_UNSUPPORTED,
                    MHA_ERR_WORKSPACE, MHA_F32, MHA_OK, LIB_PATH, MHAError, check, load, strides3)
 
-__all__ = ["attention_decode", "attention_decode_workspace_size", "attention_forward", "encoder_layer_forward", "encoder_layer_workspace_size", "linear_forward",
+__all__ = ["attention_backward", "attention_backward_workspace_size", "attention_decode",
+           "attention_decode_workspace_size", "attention_forward", "encoder_layer_forward", "encoder_layer_workspace_size", "linear_forward",
            "mha_forward", "mha_forward_workspace_size",
            "MHAError", "MHA_F32", "MHA_BF16", "LIB_PATH", "load"]
 
@@ -128,6 +129,60 @@ def attention_forward(q, k, v, *, causal: bool = False, scale: float | None = No
                                               _stream_handle(dev, stream))
     check(st)
     return (out, lse) if return_lse else out
+
+
+def attention_backward_workspace_size(batch: int, heads: int, n_q: int) -> int:
+    """Bytes of device workspace attention_backward needs (0 for invalid sizes)."""
+    return int(load().attention_backward_workspace_size(batch, heads, n_q))
+
+
+def attention_backward(q, k, v, o, d_o, lse, *, causal: bool = False, scale: float | None = None, kv_len=None,
+                       dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of attention_forward for the output gradient d_o.
+
+    q, k, v, o, d_o: (B, H, N, d) tensors as in attention_forward (any strides
+    with a contiguous last dimension); o and lse (fp32 (B, H, N_q), contiguous)
+    are what attention_forward returned for these inputs with return_lse=True,
+    the same causal flag, scale and kv_len. Returns (dq, dk, dv).
+    """
+    torch = _torch()
+    dev = _require_device(q, k, v, o, d_o)
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    if k.shape != (B, H, n_k, d) or v.shape != (B, H, n_k, d) or o.shape != q.shape or d_o.shape != q.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}, "
+                         f"o {tuple(o.shape)}, d_o {tuple(d_o.shape)}")
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n_q) \
+            or not lse.is_contiguous() or lse.device != dev:
+        raise ValueError("lse must be a contiguous float32 (B, H, N_q) tensor on the inputs' device")
+    outs = []
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            t = torch.empty(like.shape, dtype=like.dtype, device=dev)
+        _require_device(q, t)
+        if tuple(t.shape) != tuple(like.shape):
+            raise ValueError(f"{name} must have shape {tuple(like.shape)}")
+        outs.append(t)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("d_o", d_o), ("dq", outs[0]), ("dk", outs[1]),
+                    ("dv", outs[2])):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load()
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.attention_backward_workspace_size(B, H, n_q)), 16), dtype=torch.uint8,
+                                device=dev)
+    kvp = None if kv_len is None else _kv_len_arg(kv_len, B, dev)
+    st3 = [strides3(t.stride()[:3]) for t in (q, k, v, o, d_o, *outs)]
+    with _on_device(dev):
+        st = lib.attention_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), d_o.data_ptr(),
+                                    lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                    B, H, n_q, n_k, d, *st3, _dtype_code(q), int(bool(causal)), float(scale), kvp,
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream_handle(dev, stream))
+    check(st)
+    return tuple(outs)
 
 
 def linear_forward(x, w, *, out=None, stream=None):

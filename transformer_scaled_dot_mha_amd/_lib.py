@@ -53,6 +53,10 @@ SIGNATURES = {
     "encoder_layer_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int, _int, _int]),
     "encoder_layer_forward": (_int, [_vp, ctypes.POINTER(EncoderWeights), _vp, _vp, ctypes.c_size_t, _int, _int,
                                      _int, _int, _int, ctypes.c_float, _int, _int, _vp, _vp]),
+    "attention_backward_workspace_size": (ctypes.c_size_t, [_int, _int, _int]),
+    "attention_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
+                                  _i64x3, _i64x3, _i64x3, _i64x3, _i64x3, _i64x3, _i64x3, _i64x3, _int, _int,
+                                  ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
     "attention_decode_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int]),
     "attention_decode": (_int, [_vp, ctypes.POINTER(KVCache), _vp, _vp, _vp, _vp, ctypes.c_size_t, _int, _int,
                                 _int, _int, ctypes.c_float, _vp]),

@@ -55,6 +55,27 @@ struct AddNormArgs {
   float eps;
 };
 
+// Attention backward over all (batch, head) pairs: dQ, dK, dV from Q, K, V,
+// the forward output O, its gradient dO and the forward's log-sum-exp.
+// Strides in elements ({batch, head, row}, last dimension contiguous).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* d_o;
+  const float* lse;  // (batch, heads, n_q) contiguous, natural log; -inf: row with no visible key
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;      // workspace (batch, heads, n_q): rowsum(dO * O), written by the dQ launch
+  const int* kv_len;  // nullable, as in AttnArgs
+  int64_t q_s[3], k_s[3], v_s[3], o_s[3], do_s[3], dq_s[3], dk_s[3], dv_s[3];
+  int batch, heads, n_q, n_k, d;
+  int causal;
+  float scale;
+};
+
 // One decoding step: query (batch, heads, d) against the first kv_len[b] keys
 // and values of a cache (see decode.hip for the addressing). Strides in
 // elements. Partial softmax states of the key splits go to part_ml / part_o
@@ -83,6 +104,9 @@ hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_add_layernorm_bf16(const AddNormArgs& a, hipStream_t stream);
 hipError_t launch_add_layernorm_f32(const AddNormArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+// Two launches on `stream`: dQ (and delta), then dK and dV.
+hipError_t launch_attention_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attention_bwd_f32(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace mha

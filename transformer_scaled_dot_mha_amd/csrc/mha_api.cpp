@@ -45,6 +45,9 @@ bool f32_head_width(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxLdX = (int64_t)1 << 21;  // elements
 constexpr int64_t kMaxLdW = (int64_t)1 << 23;
+// Attention tiles are read through buffer descriptors whose record count
+// (bytes, 32-bit) spans up to 64 rows of the row stride.
+constexpr int64_t kMaxRowStride = (int64_t)1 << 24;  // elements
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace regions of mha_forward: Q, K, V, concatenated heads.
@@ -103,6 +106,9 @@ mha_status validate_attention(const void* q, const void* k, const void* v, void*
         return fail(MHA_ERR_INVALID_ARG, "%s stride %d (%lld) must be a multiple of %d elements", names[t],
                     i, (long long)strides[t][i], vec);
     }
+    if (strides[t][2] > kMaxRowStride)
+      return fail(MHA_ERR_UNSUPPORTED, "%s row stride (%lld) exceeds %lld elements", names[t],
+                  (long long)strides[t][2], (long long)kMaxRowStride);
   }
   // grid: one workgroup per (batch, head, 64- or 128-row query block)
   const int64_t blocks = (int64_t)batch * heads * ((n_q + 63) / 64);
@@ -422,6 +428,61 @@ mha_status decode_impl(const void* q, const mha_kv_cache* cache, const int32_t* 
   return hip_status(e, "decode launch");
 }
 
+mha_status backward_impl(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                         void* dq, void* dk, void* dv, int batch, int heads, int n_q, int n_k, int d,
+                         const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                         const int64_t* o_strides, const int64_t* do_strides, const int64_t* dq_strides,
+                         const int64_t* dk_strides, const int64_t* dv_strides, mha_dtype dtype, int causal,
+                         float scale, const int32_t* kv_len, void* workspace, size_t workspace_bytes, void* stream) {
+  // the forward's rules cover q, k, v and o; then the gradient tensors
+  mha_status s = validate_attention(q, k, v, const_cast<void*>(o), batch, heads, n_q, n_k, d, d, q_strides, k_strides,
+                                    v_strides, o_strides, (int)dtype, causal, scale);
+  if (s != MHA_OK) return s;
+  if (!d_o || !dq || !dk || !dv || !lse || !workspace)
+    return fail(MHA_ERR_INVALID_ARG, "d_o, dq, dk, dv, lse and workspace must be non-null");
+  if (!do_strides || !dq_strides || !dk_strides || !dv_strides)
+    return fail(MHA_ERR_INVALID_ARG, "stride arrays must be non-null");
+  const int vec = vec_elems(dtype);
+  const void* ptrs[4] = {d_o, dq, dk, dv};
+  const char* names[4] = {"d_o", "dq", "dk", "dv"};
+  const int64_t* strides[4] = {do_strides, dq_strides, dk_strides, dv_strides};
+  for (int t = 0; t < 4; ++t) {
+    if (!aligned16(ptrs[t])) return fail(MHA_ERR_INVALID_ARG, "%s must be 16-byte aligned", names[t]);
+    for (int i = 0; i < 3; ++i) {
+      if (strides[t][i] < 0) return fail(MHA_ERR_INVALID_ARG, "%s stride %d is negative", names[t], i);
+      if (strides[t][i] % vec)
+        return fail(MHA_ERR_INVALID_ARG, "%s stride %d (%lld) must be a multiple of %d elements", names[t], i,
+                    (long long)strides[t][i], vec);
+    }
+    if (strides[t][2] > kMaxRowStride)
+      return fail(MHA_ERR_UNSUPPORTED, "%s row stride (%lld) exceeds %lld elements", names[t],
+                  (long long)strides[t][2], (long long)kMaxRowStride);
+  }
+  if (!aligned16(lse) || !aligned16(workspace)) return fail(MHA_ERR_INVALID_ARG, "lse and workspace must be 16-byte aligned");
+  if (kv_len && !aligned4(kv_len)) return fail(MHA_ERR_INVALID_ARG, "kv_len must be 4-byte aligned");
+  const size_t need = round_up((size_t)batch * heads * n_q * 4);
+  if (workspace_bytes < need)
+    return fail(MHA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  const int64_t kblocks = (int64_t)batch * heads * ((n_k + 63) / 64);
+  if (kblocks > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "too many (batch, head, key block) triples");
+
+  mha::BwdArgs a = {};
+  a.q = q, a.k = k, a.v = v, a.o = o, a.d_o = d_o, a.lse = lse;
+  a.dq = dq, a.dk = dk, a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  a.kv_len = kv_len;
+  for (int i = 0; i < 3; ++i) {
+    a.q_s[i] = q_strides[i], a.k_s[i] = k_strides[i], a.v_s[i] = v_strides[i], a.o_s[i] = o_strides[i];
+    a.do_s[i] = do_strides[i], a.dq_s[i] = dq_strides[i], a.dk_s[i] = dk_strides[i], a.dv_s[i] = dv_strides[i];
+  }
+  a.batch = batch, a.heads = heads, a.n_q = n_q, a.n_k = n_k, a.d = d;
+  a.causal = causal;
+  a.scale = scale;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == MHA_BF16 ? mha::launch_attention_bwd_bf16(a, st) : mha::launch_attention_bwd_f32(a, st);
+  return hip_status(e, "attention backward launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -439,7 +500,7 @@ const char* mha_status_string(mha_status s) {
 
 const char* mha_last_error(void) { return g_last_error.c_str(); }
 
-int mha_version(void) { return 300; }
+int mha_version(void) { return 400; }
 
 mha_status attention_forward(const void* q, const void* k, const void* v, void* o, int batch, int heads,
                              int n_q, int n_k, int d_k, int d_v, const int64_t q_strides[3],
@@ -553,6 +614,29 @@ mha_status attention_decode(const void* q, const mha_kv_cache* cache, const int3
     return decode_impl(q, cache, kv_len, o, lse, workspace, workspace_bytes, batch, heads, d, dtype, scale, stream);
   } catch (...) {
     return fail(MHA_ERR_HIP, "internal error in attention_decode");
+  }
+}
+
+size_t attention_backward_workspace_size(int batch, int heads, int n_q) {
+  if (batch < 1 || heads < 1 || n_q < 1) return 0;
+  const unsigned __int128 bytes = (unsigned __int128)batch * heads * n_q * 4;
+  if (bytes > ((unsigned __int128)1 << 62)) return 0;
+  return round_up((size_t)bytes);
+}
+
+mha_status attention_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                              const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int n_q, int n_k,
+                              int d, const int64_t q_strides[3], const int64_t k_strides[3],
+                              const int64_t v_strides[3], const int64_t o_strides[3], const int64_t do_strides[3],
+                              const int64_t dq_strides[3], const int64_t dk_strides[3], const int64_t dv_strides[3],
+                              mha_dtype dtype, int causal, float scale, const int32_t* kv_len, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  try {
+    return backward_impl(q, k, v, o, d_o, lse, dq, dk, dv, batch, heads, n_q, n_k, d, q_strides, k_strides, v_strides,
+                         o_strides, do_strides, dq_strides, dk_strides, dv_strides, dtype, causal, scale, kv_len,
+                         workspace, workspace_bytes, stream);
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in attention_backward");
   }
 }
 
