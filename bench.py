@@ -9,7 +9,9 @@ N = 512, d_model = 512, h = 8, d_k = 64, no mask; a step is one mha_forward
 (Q/K/V projections, attention, W^O). Attention-only workloads
 (--workload decoder|cross|long) time one attention_forward per step;
 --workload decode times one attention_decode (one query per (batch, head)
-against a paged K/V cache), reported against the HBM roofline.
+against a paged K/V cache), reported against the HBM roofline; --workload bwd
+times one attention_backward of the long causal attention (FLOPs counted as
+10*H*d per unmasked pair, 2.5x the forward's).
 
 Prints ONE JSON line. `value` is algorithmic TFLOP/s of the step (FLOPs =
 4*B*H*d*unmasked pairs for attention, 2*m*n*k per projection) with inputs
@@ -45,6 +47,7 @@ KERNEL_SOURCES = {
     "attention": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_bf16.hip"),
     "linear": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "linear_bf16.hip"),
     "decode": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "decode.hip"),
+    "backward": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_bwd_bf16.hip"),
 }
 
 
@@ -106,6 +109,30 @@ def cpu_baseline(w, inputs, min_seconds=10.0, max_seconds=30.0):
     import oracle
     info = threadpoolctl.threadpool_info()
     threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    if w.kind == "bwd":
+        # whole (batch, head) pairs at full length, one at a time, until ~min_seconds
+        per_pair = 10 * w.d_k * (w.total_pairs() // w.batch)
+        qv, kv, vv, dv = (inputs[n].value for n in ("q", "k", "v", "do"))
+        done = []
+        t0 = time.perf_counter()
+        for b in range(w.batch):
+            for h in range(w.heads):
+                g = oracle.attention_backward_ref(qv[b:b + 1, h:h + 1], kv[b:b + 1, h:h + 1], vv[b:b + 1, h:h + 1],
+                                                  dv[b:b + 1, h:h + 1], causal=w.causal)
+                done.append(((b, h), g))
+                el = time.perf_counter() - t0
+                if el >= min_seconds or el + el / len(done) > max_seconds:
+                    break
+            else:
+                continue
+            break
+        el = time.perf_counter() - t0
+        return {"value": round(per_pair * len(done) / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+                "kind": "oracle",
+                "sample": f"{len(done)} whole (batch, head) pair(s) of the workload at full length, "
+                          f"oracle.attention_backward_ref in float64; {el:.1f} s",
+                "host_cpus": os.cpu_count(),
+                "blas": ",".join(sorted({d.get("internal_api", "?") for d in info}))}, done
     if w.kind == "decode":
         fn = lambda: oracle.decode_ref(inputs["q"].value, inputs["k"].value, inputs["v"].value, w.kv_lengths())
         flops = w.attention_flops()
@@ -154,7 +181,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="encoder",
-                    help="encoder | tiny | decoder | cross | long | padded | layer | decode")
+                    help="encoder | tiny | decoder | cross | long | padded | layer | decode | bwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the long causal attention line")
     ap.add_argument("--calib-copy", action="store_true",
@@ -181,7 +208,31 @@ def main():
     result = {}
     lens = w.kv_lengths()
     kv_len = None if lens is None else torch.from_numpy(lens).to(dev)
-    if w.kind == "decode":
+    if w.kind == "bwd":
+        q, k, v, do = (torch_tensor(inputs[n], dev) for n in ("q", "k", "v", "do"))
+        # the forward's output and log-sum-exp, saved once as training saves them
+        o, lse = mha.attention_forward(q, k, v, causal=w.causal, return_lse=True)
+        esz = q.element_size()
+        per_set = 8 * q.numel() * esz
+        n_sets = max(1, math.ceil(ROTATE_BYTES / per_set))
+        sets = [(q, k, v, o, do)] + [tuple(t.clone() for t in (q, k, v, o, do)) for _ in range(n_sets - 1)]
+        grads = [tuple(torch.empty_like(t) for t in (q, k, v)) for _ in range(n_sets)]
+        work = torch.empty(mha.attention_backward_workspace_size(w.batch, w.heads, w.n_q), dtype=torch.uint8,
+                           device=dev)
+
+        def step(i):
+            qi, ki, vi, oi, doi = sets[i % n_sets]
+            dq, dk, dv = grads[i % n_sets]
+            mha.attention_backward(qi, ki, vi, oi, doi, lse, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=work)
+
+        step(0)
+        torch.cuda.synchronize()
+        flops_step = w.backward_flops()
+        # the step is the backward itself: the dQ launch, then the dK/dV launch
+        dom_fn, dom_flops, dom_name = step, flops_step, "attn_bwd_dq_bf16+attn_bwd_dkdv_bf16"
+        dom_bytes = per_set
+        get_out = lambda: grads[0]
+    elif w.kind == "decode":
         table_np, num_pages = w.pages()
         q = torch_tensor(inputs["q"], dev)
         # pages stored head-major, (num_pages, H, P, d), passed as a (pages, slots, H, d) view
@@ -310,7 +361,8 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     launch_desc = f"{dom_name}:{w.name}"
-    src_key = "linear" if dom_name.startswith("linear") else "decode" if dom_name.startswith("decode") else "attention"
+    src_key = ("linear" if dom_name.startswith("linear") else "decode" if dom_name.startswith("decode")
+               else "backward" if dom_name.startswith("attn_bwd") else "attention")
     gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
     if w.kind == "decode":
         # one query row: 2 flops per byte-pair of K/V, far below the MFMA ridge -- HBM-bound
@@ -325,6 +377,10 @@ def main():
                     "traffic": traffic_for(src_key, launch_desc),
                     "algorithmic_bytes": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
                     "achieved_gbps": round(gbps, 1)}
+        if w.kind == "bwd":
+            # the two launches recompute S and dP to avoid atomics: 7 products per pair, 5 counted
+            roofline["executed_tflops"] = round(achieved * 14 / 10, 2)
+            roofline["launches_per_step"] = 2
     log(f"dominant kernel {dom_name}: {dom_ms * 1e3:.1f} us, {achieved:.1f} TFLOP/s, {gbps:.0f} GB/s")
 
     secondary = None
@@ -354,11 +410,15 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host cores")
         cpu, ref = cpu_baseline(w, inputs)
-        got = get_out().float().cpu().numpy().astype(np.float64)
-        if w.kind == "attn" and w.oracle_rows:
-            got = got[:, :, workloads.sample_rows(w)]
-        ref_o = ref if w.kind in ("mha", "layer") else ref[0]
-        err = float(np.max(np.abs(got - ref_o)))
+        if w.kind == "bwd":
+            outs = [t.float().cpu().numpy().astype(np.float64) for t in get_out()]
+            err = max(float(np.max(np.abs(outs[i][b, h] - g[i][0, 0]))) for (b, h), g in ref for i in range(3))
+        else:
+            got = get_out().float().cpu().numpy().astype(np.float64)
+            if w.kind == "attn" and w.oracle_rows:
+                got = got[:, :, workloads.sample_rows(w)]
+            ref_o = ref if w.kind in ("mha", "layer") else ref[0]
+            err = float(np.max(np.abs(got - ref_o)))
         result["parity_max_abs"] = err
         log(f"parity vs oracle: max-abs {err:.3e}")
 
@@ -369,6 +429,8 @@ def main():
                              "LayerNorm",
                     "decode": "attention_decode: one query per (batch, head) against the paged K/V cache "
                               "(two launches: the key splits, then their merge)",
+                    "bwd": "attention_backward: dQ, dK, dV of causal attention for a given dO, from the "
+                           "forward's saved O and log-sum-exp (two launches: dQ, then dK/dV)",
                     }.get(w.kind, "attention_forward")}
     if w.kind in ("mha", "layer"):
         cfg["d_model"] = w.d_model
@@ -380,7 +442,10 @@ def main():
     if lens is not None:
         cfg["kv_len"] = (f"per-batch key lengths uniform in [{w.kv_len_range[0]}, {w.kv_len_range[1]}] "
                          f"(seeded; mean {float(lens.mean()):.1f})")
-    line = {"metric": "attention fwd TFLOP/s and % of bf16 MFMA peak at 1 GPU (h=8, d_k=64)",
+    metric = "attention fwd TFLOP/s and % of bf16 MFMA peak at 1 GPU (h=8, d_k=64)"
+    if w.kind == "bwd":
+        metric = "attention bwd TFLOP/s (10*H*d per unmasked pair) and % of bf16 MFMA peak at 1 GPU"
+    line = {"metric": metric,
             "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg,

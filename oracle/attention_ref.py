@@ -211,6 +211,57 @@ def attention_backward_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.n
     return dq, dk, dv
 
 
+def attention_backward_sampled_ref(q, k, v, do, rows, keys, *, causal: bool = False, scale: float | None = None,
+                                   kv_len=None, chunk: int = 512):
+    """attention_backward_ref restricted to query rows `rows` (dQ) and key rows
+    `keys` (dK, dV), for sizes where the full score matrix is too large.
+
+    The softmax statistics come from the forward oracle, chunk by chunk of
+    query rows: lse_i, and delta_i = dO_i . O_i (equal to sum_j P_ij dP_ij,
+    since O_i = sum_j P_ij V_j). Then dQ_i = scale sum_j dS_ij K_j over a
+    sampled row, and dV_j = sum_i P_ij dO_i, dK_j = scale sum_i dS_ij Q_i over
+    a sampled key column, with P_ij = exp(scale q_i.k_j - lse_i) and
+    dS_ij = P_ij (dO_i . V_j - delta_i). Returns (dQ (B,H,R,d), dK (B,H,C,d),
+    dV (B,H,C,d)) for the R rows and C keys."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows, keys = np.asarray(rows), np.asarray(keys)
+    lse = np.empty((B, H, n_q))
+    delta = np.empty((B, H, n_q))
+    for c0 in range(0, n_q, chunk):
+        r = np.arange(c0, min(c0 + chunk, n_q))
+        o, _, l = attention_ref(q, k, v, causal=causal, scale=scale, rows=r, kv_len=kv_len)
+        lse[:, :, r] = l
+        delta[:, :, r] = np.sum(do[:, :, r] * o, axis=-1)
+    dq = np.zeros((B, H, len(rows), d))
+    dk = np.zeros((B, H, len(keys), d))
+    dv = np.zeros((B, H, len(keys), v.shape[-1]))
+    for b in range(B):
+        length = n_k if kv_len is None else min(max(int(kv_len[b]), 0), n_k)
+        for h in range(H):
+            # sampled rows: every key
+            s = np.matmul(q[b, h][rows], k[b, h].T) * scale
+            vis = np.arange(n_k)[None, :] < length
+            if causal:
+                vis = vis & (np.arange(n_k)[None, :] <= rows[:, None])
+            p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse[b, h][rows][:, None]), 0.0)
+            ds = p * (np.matmul(do[b, h][rows], v[b, h].T) - delta[b, h][rows][:, None])
+            dq[b, h] = scale * np.matmul(ds, k[b, h])
+            # sampled keys: every query
+            s = np.matmul(q[b, h], k[b, h][keys].T) * scale
+            vis = np.broadcast_to(keys[None, :] < length, s.shape)
+            if causal:
+                vis = vis & (keys[None, :] <= np.arange(n_q)[:, None])
+            p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse[b, h][:, None]), 0.0)
+            ds = p * (np.matmul(do[b, h], v[b, h][keys].T) - delta[b, h][:, None])
+            dv[b, h] = np.matmul(p.T, do[b, h])
+            dk[b, h] = scale * np.matmul(ds.T, q[b, h])
+    return dq, dk, dv
+
+
 def causal_mask_rows(n: int, rows) -> np.ndarray:
     """The rows `rows` of causal_mask(n), formed without the full n x n matrix."""
     rows = np.asarray(rows)

@@ -740,6 +740,24 @@ def check_backward_saturation(bwd):
     routed[perm] = do[0, 0]                 # key perm[i] receives query i's dO row
     assert np.allclose(frozen[2][0, 0], routed, atol=1e-12), "dV routes dO rows through the one-hot weights"
 
+
+def check_backward_sampled(sampled, bwd):
+    """The sampled backward (statistics from the forward, delta as dO . O)
+    equals the full backward on the sampled rows and keys, for every mask;
+    rows with no visible key and padded keys give 0."""
+    r = _rng(77)
+    B, H, n, d = 2, 2, 37, 5
+    q, k, v, do = (r.standard_normal((B, H, n, d)) for _ in range(4))
+    rows = np.array([0, 1, 17, 35, 36])
+    keys = np.array([0, 2, 20, 30, 36])
+    for causal, kv_len in ((False, None), (True, None), (False, [37, 21]), (True, [0, 25])):
+        full = bwd(q, k, v, do, causal=causal, kv_len=kv_len)
+        part = sampled(q, k, v, do, rows, keys, causal=causal, kv_len=kv_len, chunk=8)
+        assert np.allclose(part[0], full[0][:, :, rows], rtol=0, atol=1e-12), f"sampled dQ ({causal}, {kv_len})"
+        assert np.allclose(part[1], full[1][:, :, keys], rtol=0, atol=1e-12), f"sampled dK ({causal}, {kv_len})"
+        assert np.allclose(part[2], full[2][:, :, keys], rtol=0, atol=1e-12), f"sampled dV ({causal}, {kv_len})"
+
+
 ATTENTION_PINS = [check_rows_sum_to_one, check_permutation_equivariance,
                   check_constant_v_and_convex_hull, check_causal_locality,
                   check_masked_weight_is_zero, check_closed_forms, check_low_temperature_argmax,

@@ -153,3 +153,24 @@ def test_backward_gradient_check_on_gpu(dev):
     an = float(sum((gg.double() * u.double()).sum() for gg, u in zip((gq, gk, gv), dirs)))
     torch.cuda.synchronize()
     assert abs(fd - an) <= 1e-3 * max(1.0, abs(an)), f"directional derivative {fd} vs gradients {an}"
+
+
+def test_backward_workload_parity(dev):
+    """The timed backward workload (long causal, B=2, H=16, N=8192) at full size
+    in the bench's launch configuration, against the oracle on 64 sampled query
+    rows (dQ) and the same 64 key rows (dK, dV) of every (batch, head); the
+    softmax statistics behind them cover all 8192 rows."""
+    import torch
+    w = workloads.get("bwd")
+    x = workloads.make_inputs(w)
+    q, k, v, do = (to_device(x[n], dev) for n in ("q", "k", "v", "do"))
+    say(f"backward workload {w.name}")
+    o, lse = mha.attention_forward(q, k, v, causal=True, return_lse=True)
+    dq, dk, dv = mha.attention_backward(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    rows = workloads.sample_rows(w)
+    want = oracle.attention_backward_sampled_ref(x["q"].value, x["k"].value, x["v"].value, x["do"].value, rows, rows,
+                                                 causal=True)
+    idx = torch.from_numpy(rows).to(dev)
+    got = tuple(t.index_select(2, idx) for t in (dq, dk, dv))
+    check_grads(got, want, "bf16", "backward workload")

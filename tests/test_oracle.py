@@ -128,3 +128,7 @@ def test_backward_invariants():
 
 def test_backward_saturation():
     pins.check_backward_saturation(oracle.attention_backward_ref)
+
+
+def test_backward_sampled():
+    pins.check_backward_sampled(oracle.attention_backward_sampled_ref, oracle.attention_backward_ref)

@@ -31,7 +31,8 @@ class Workload:
     name: str
     kind: str            # "mha": projections + attention + W^O;  "attn": attention core only;
                          # "layer": a whole encoder layer (attention sub-layer, FFN, two residual norms);
-                         # "decode": one query per (batch, head) against a K/V cache of n_k slots
+                         # "decode": one query per (batch, head) against a K/V cache of n_k slots;
+                         # "bwd": the attention backward (dQ, dK, dV for a given dO)
     dtype: str           # "f32" or "bf16": the stored type of every tensor
     batch: int
     heads: int
@@ -89,6 +90,12 @@ class Workload:
         """4 * H * d * (unmasked pairs over the batch): QK^T and PV, two flops per multiply-add."""
         return 4 * self.heads * self.d_k * self.total_pairs()
 
+    def backward_flops(self) -> int:
+        """10 * H * d * (unmasked pairs): the five products of the gradient (dV = P^T dO,
+        dP = dO V^T, dQ = dS K, dK = dS^T Q, and S = Q K^T again for P), two flops per
+        multiply-add -- 2.5 times the forward's count."""
+        return 10 * self.heads * self.d_k * self.total_pairs()
+
     def projection_flops(self) -> int:
         if self.kind not in ("mha", "layer"):
             return 0
@@ -105,6 +112,8 @@ class Workload:
         return 2 * 2 * self.batch * self.n_q * self.d_model * self.d_ff
 
     def total_flops(self) -> int:
+        if self.kind == "bwd":
+            return self.backward_flops()
         return self.attention_flops() + self.projection_flops() + self.ffn_flops()
 
 
@@ -130,6 +139,9 @@ WORKLOADS: dict[str, Workload] = {
         # one decoding step of the base model (8 heads of 64) for 64 sequences against a
         # paged K/V cache of 16-slot pages, each page stored head-major (H, 16, d);
         # cached lengths uniform in [1024, 4096]
+        # the backward of the long causal attention (training at long context)
+        Workload("long_causal_bwd_bf16_b2_h16_n8192", "bwd", "bf16", batch=2, heads=16,
+                 n_q=8192, n_k=8192, d_k=64, causal=True, seed=9, oracle_rows=64),
         Workload("decode_paged_bf16_b64_h8_kv4096", "decode", "bf16", batch=64, heads=8,
                  n_q=1, n_k=4096, d_k=64, causal=False, seed=8, kv_len_range=(1024, 4096), page_size=16),
     ]
@@ -145,6 +157,7 @@ ALIASES = {
     "padded": "base_encoder_padded_mha_bf16_b32_n512",
     "layer": "base_encoder_layer_bf16_b32_n512",
     "decode": "decode_paged_bf16_b64_h8_kv4096",
+    "bwd": "long_causal_bwd_bf16_b2_h16_n8192",
 }
 
 
@@ -215,6 +228,7 @@ def make_inputs(w: Workload, *, v_ones: bool = False) -> dict[str, Stored]:
     layer: x (B, N, d_model), then encoder_params(d_model, d_ff, seed=100 + seed).
     attn: Q (B, H, N_q, d), K (B, H, N_k, d), V (B, H, N_k, d).
     decode: Q (B, H, d), then the logical caches K (B, H, N_k, d), V (B, H, N_k, d).
+    bwd: Q, K, V as for attn, then dO (B, H, N_q, d).
     v_ones replaces V by all ones after drawing (row-sum checks); the draws
     themselves are unchanged so Q and K stay identical to the plain run.
     """
@@ -238,6 +252,8 @@ def make_inputs(w: Workload, *, v_ones: bool = False) -> dict[str, Stored]:
     if v_ones:
         v = np.ones_like(v)
     out["v"] = store(v, w.dtype)
+    if w.kind == "bwd":
+        out["do"] = store(rng.standard_normal((w.batch, w.heads, w.n_q, w.d_v)), w.dtype)
     return out
 
 
