@@ -156,7 +156,7 @@ def attention_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool =
 
 
 def attention_backward_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, *, causal: bool = False,
-                           scale: float | None = None, kv_len=None):
+                           scale: float | None = None, kv_len=None, error_scale: bool = False):
     """Gradients of the attention output with respect to Q, K and V.
 
     The pages motivate the 1/sqrt(d_k) scale by the gradient that flows back
@@ -177,6 +177,13 @@ def attention_backward_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.n
     weights are 0 and so is dS there. A row with no visible key has P = 0 and
     passes nothing. q, k, do: as in attention_ref; returns (dQ, dK, dV) of the
     shapes of q, k and v, in float64.
+
+    error_scale: also return (E_dQ, E_dK, E_dV), the sums of the absolute
+    values of the terms each gradient element adds up -- the scale that
+    rounding errors in those terms are proportional to (for tests):
+      E_dV = P^T |dO|,  g_ij = |dS_ij| + P_ij sum_d |dO_id O_id|,
+      E_dQ = |scale| g |K|,  E_dK = |scale| g^T |Q|.
+    The second part of g covers delta, whose terms are dO_id O_id.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -191,6 +198,7 @@ def attention_backward_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.n
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    eq, ek, ev = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for b in range(B):
         for h in range(H):
             s = np.matmul(q[b, h], k[b, h].T) * scale
@@ -208,11 +216,19 @@ def attention_backward_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.n
             dv[b, h] = np.matmul(p.T, do[b, h])
             dq[b, h] = scale * np.matmul(ds, k[b, h])
             dk[b, h] = scale * np.matmul(ds.T, q[b, h])
+            if error_scale:
+                o = np.matmul(p, v[b, h])
+                g = np.abs(ds) + p * np.sum(np.abs(do[b, h] * o), axis=-1, keepdims=True)
+                ev[b, h] = np.matmul(p.T, np.abs(do[b, h]))
+                eq[b, h] = abs(scale) * np.matmul(g, np.abs(k[b, h]))
+                ek[b, h] = abs(scale) * np.matmul(g.T, np.abs(q[b, h]))
+    if error_scale:
+        return dq, dk, dv, (eq, ek, ev)
     return dq, dk, dv
 
 
 def attention_backward_sampled_ref(q, k, v, do, rows, keys, *, causal: bool = False, scale: float | None = None,
-                                   kv_len=None, chunk: int = 512):
+                                   kv_len=None, chunk: int = 512, error_scale: bool = False):
     """attention_backward_ref restricted to query rows `rows` (dQ) and key rows
     `keys` (dK, dV), for sizes where the full score matrix is too large.
 
@@ -222,7 +238,8 @@ def attention_backward_sampled_ref(q, k, v, do, rows, keys, *, causal: bool = Fa
     sampled row, and dV_j = sum_i P_ij dO_i, dK_j = scale sum_i dS_ij Q_i over
     a sampled key column, with P_ij = exp(scale q_i.k_j - lse_i) and
     dS_ij = P_ij (dO_i . V_j - delta_i). Returns (dQ (B,H,R,d), dK (B,H,C,d),
-    dV (B,H,C,d)) for the R rows and C keys."""
+    dV (B,H,C,d)) for the R rows and C keys, and with error_scale the term
+    magnitudes of attention_backward_ref for them."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     B, H, n_q, d = q.shape
     n_k = k.shape[2]
@@ -231,14 +248,17 @@ def attention_backward_sampled_ref(q, k, v, do, rows, keys, *, causal: bool = Fa
     rows, keys = np.asarray(rows), np.asarray(keys)
     lse = np.empty((B, H, n_q))
     delta = np.empty((B, H, n_q))
+    dabs = np.empty((B, H, n_q))
     for c0 in range(0, n_q, chunk):
         r = np.arange(c0, min(c0 + chunk, n_q))
         o, _, l = attention_ref(q, k, v, causal=causal, scale=scale, rows=r, kv_len=kv_len)
         lse[:, :, r] = l
         delta[:, :, r] = np.sum(do[:, :, r] * o, axis=-1)
+        dabs[:, :, r] = np.sum(np.abs(do[:, :, r] * o), axis=-1)
     dq = np.zeros((B, H, len(rows), d))
     dk = np.zeros((B, H, len(keys), d))
     dv = np.zeros((B, H, len(keys), v.shape[-1]))
+    eq, ek, ev = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
     for b in range(B):
         length = n_k if kv_len is None else min(max(int(kv_len[b]), 0), n_k)
         for h in range(H):
@@ -250,6 +270,9 @@ def attention_backward_sampled_ref(q, k, v, do, rows, keys, *, causal: bool = Fa
             p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse[b, h][rows][:, None]), 0.0)
             ds = p * (np.matmul(do[b, h][rows], v[b, h].T) - delta[b, h][rows][:, None])
             dq[b, h] = scale * np.matmul(ds, k[b, h])
+            if error_scale:
+                g = np.abs(ds) + p * dabs[b, h][rows][:, None]
+                eq[b, h] = abs(scale) * np.matmul(g, np.abs(k[b, h]))
             # sampled keys: every query
             s = np.matmul(q[b, h], k[b, h][keys].T) * scale
             vis = np.broadcast_to(keys[None, :] < length, s.shape)
@@ -259,6 +282,12 @@ def attention_backward_sampled_ref(q, k, v, do, rows, keys, *, causal: bool = Fa
             ds = p * (np.matmul(do[b, h], v[b, h][keys].T) - delta[b, h][:, None])
             dv[b, h] = np.matmul(p.T, do[b, h])
             dk[b, h] = scale * np.matmul(ds.T, q[b, h])
+            if error_scale:
+                g = np.abs(ds) + p * dabs[b, h][:, None]
+                ev[b, h] = np.matmul(p.T, np.abs(do[b, h]))
+                ek[b, h] = abs(scale) * np.matmul(g.T, np.abs(q[b, h]))
+    if error_scale:
+        return dq, dk, dv, (eq, ek, ev)
     return dq, dk, dv
 
 

@@ -758,6 +758,31 @@ def check_backward_sampled(sampled, bwd):
         assert np.allclose(part[2], full[2][:, :, keys], rtol=0, atol=1e-12), f"sampled dV ({causal}, {kv_len})"
 
 
+
+def check_backward_error_scale(bwd, sampled):
+    """The term magnitudes bound the gradients (|sum| <= sum |terms|), equal
+    them where every term is non-negative (dV with dO >= 0), are 0 exactly
+    where no term exists (padded keys, empty rows), and agree between the full
+    and the sampled oracle."""
+    r = _rng(78)
+    B, H, n, d = 2, 2, 21, 4
+    q, k, v = (r.standard_normal((B, H, n, d)) for _ in range(3))
+    do = r.standard_normal((B, H, n, d))
+    for causal, kv_len in ((False, None), (True, [21, 0])):
+        *g, e = bwd(q, k, v, do, causal=causal, kv_len=kv_len, error_scale=True)
+        for gi, ei in zip(g, e):
+            assert np.all(np.abs(gi) <= ei + 1e-12), "term magnitudes bound the gradient"
+        rows = keys = np.array([0, 5, 20])
+        *gs, es = sampled(q, k, v, do, rows, keys, causal=causal, kv_len=kv_len, chunk=8, error_scale=True)
+        for ei, esi, idx in zip(e, es, (rows, keys, keys)):
+            assert np.allclose(esi, ei[:, :, idx], rtol=0, atol=1e-12), "sampled term magnitudes"
+    *g, e = bwd(q, k, v, np.abs(do), error_scale=True)
+    assert np.allclose(e[2], g[2], atol=1e-12), "dV with dO >= 0: magnitude equals the gradient"
+    *g, e = bwd(q, k, v, do, kv_len=[7, 0], error_scale=True)
+    assert np.all(e[1][0, :, 7:] == 0) and np.all(e[2][0, :, 7:] == 0), "padded keys: no terms"
+    assert all(np.all(x[1] == 0) for x in e), "no visible key: no terms"
+
+
 ATTENTION_PINS = [check_rows_sum_to_one, check_permutation_equivariance,
                   check_constant_v_and_convex_hull, check_causal_locality,
                   check_masked_weight_is_zero, check_closed_forms, check_low_temperature_argmax,

@@ -132,3 +132,7 @@ def test_backward_saturation():
 
 def test_backward_sampled():
     pins.check_backward_sampled(oracle.attention_backward_sampled_ref, oracle.attention_backward_ref)
+
+
+def test_backward_error_scale():
+    pins.check_backward_error_scale(oracle.attention_backward_ref, oracle.attention_backward_sampled_ref)

@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace mha {
@@ -88,16 +90,17 @@ __device__ __forceinline__ u32x4 gather_row_chunk(unsigned a0, unsigned a1, unsi
 }
 
 // Store a 32-row x 64 block held transposed in two accumulators (lane: row
-// l%32, d = 32*blk + 8*g + 4*hf + 0..3), times `mul`, as bf16 rows.
+// l%32, d = 32*blk + 8*g + 4*hf + 0..3), times `mul`, as bf16 rows; a lane
+// with `zero` set stores zeros whatever its accumulators hold.
 __device__ __forceinline__ void store_rows(bf16* row_ptr, bool ok, const f32x16& a0, const f32x16& a1, float mul,
-                                           int hf) {
+                                           int hf, bool zero = false) {
   unsigned w[2][4][2];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    w[0][g][0] = pack_bf16(a0[4 * g] * mul, a0[4 * g + 1] * mul);
-    w[0][g][1] = pack_bf16(a0[4 * g + 2] * mul, a0[4 * g + 3] * mul);
-    w[1][g][0] = pack_bf16(a1[4 * g] * mul, a1[4 * g + 1] * mul);
-    w[1][g][1] = pack_bf16(a1[4 * g + 2] * mul, a1[4 * g + 3] * mul);
+    w[0][g][0] = zero ? 0u : pack_bf16(a0[4 * g] * mul, a0[4 * g + 1] * mul);
+    w[0][g][1] = zero ? 0u : pack_bf16(a0[4 * g + 2] * mul, a0[4 * g + 3] * mul);
+    w[1][g][0] = zero ? 0u : pack_bf16(a1[4 * g] * mul, a1[4 * g + 1] * mul);
+    w[1][g][1] = zero ? 0u : pack_bf16(a1[4 * g + 2] * mul, a1[4 * g + 3] * mul);
   }
   u32x4 chunk[2][2];
 #pragma unroll
@@ -232,49 +235,67 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16(BwdArgs a, float c, i
     vs.store_rows(base + 2 * kTileElems, vr);
   };
 
+  // One 64-key tile. Tiles that straddle the causal diagonal or hold the end
+  // of the keys mask their pairs (a key past n_k is a zero row, but its
+  // unmasked weight exp(-lse) can overflow); the others need no mask.
+  auto tile = [&](int k0, const bf16* Ks, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
+    const bf16* Kt = Ks + kTileElems;
+    const bf16* Vs = Ks + 2 * kTileElems;
+    // keys of this lane's registers: k0 + 32*slab + acc_row(r, hf)
+    const int last = (kCausal ? min(n_k - 1, my_q) : n_k - 1) - k0;
+#pragma unroll
+    for (int slab = 0; slab < 2; ++slab) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        s = mfma(s, ld16(Ks + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf), qf[kk]);
+        dp = mfma(dp, ld16(Vs + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf), dof[kk]);
+      }
+      unsigned pw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float ds2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * i + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+          if (kMasked) p = 32 * slab + acc_row(r, hf) <= last ? p : 0.f;
+          ds2[e] = p * (dp[r] - delta);
+        }
+        pw[i] = pack_bf16(ds2[0], ds2[1]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x4 bs = u32x4{pw[4 * jj], pw[4 * jj + 1], pw[4 * jj + 2], pw[4 * jj + 3]};
+        dq0 = mfma(dq0, ld16(Kt + lq * kPitch + 16 * (2 * slab + jj) + 8 * hf), bs);
+        dq1 = mfma(dq1, ld16(Kt + (32 + lq) * kPitch + 16 * (2 * slab + jj) + 8 * hf), bs);
+      }
+    }
+  };
+
   if (ntiles > 0) {
     gload(0);
     lstore(0);
   }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  // tiles before t_split lie wholly below every query of the workgroup and
+  // before the end of the keys
+  const int t_split = min(kCausal ? qblk * (128 / kBlk) : ntiles, n_k / kBlk);
+  int t = 0;
+  for (; t < t_split; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) gload((t + 1) * kBlk);
+    tile(t * kBlk, smem + (t & 1) * 3 * kTileElems, std::false_type());
+    if (more) lstore((t + 1) & 1);
+    __syncthreads();
+  }
+  for (; t < ntiles; ++t) {
     const int k0 = t * kBlk;
     const bool more = t + 1 < ntiles;
     if (more) gload(k0 + kBlk);
-    const bf16* Ks = smem + (t & 1) * 3 * kTileElems;
-    const bf16* Kt = Ks + kTileElems;
-    const bf16* Vs = Ks + 2 * kTileElems;
-    if (!kCausal || k0 <= q_wave0 + 31) {  // uniform over the wavefront
-      // keys of this lane's registers are k0 + 32*slab + acc_row(r, hf)
-      const int last = (kCausal ? min(n_k - 1, my_q) : n_k - 1) - k0;
-#pragma unroll
-      for (int slab = 0; slab < 2; ++slab) {
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          s = mfma(s, ld16(Ks + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf), qf[kk]);
-          dp = mfma(dp, ld16(Vs + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf), dof[kk]);
-        }
-        unsigned pw[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float ds2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * i + e;
-            const float p = 32 * slab + acc_row(r, hf) <= last ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2)) : 0.f;
-            ds2[e] = p * (dp[r] - delta);
-          }
-          pw[i] = pack_bf16(ds2[0], ds2[1]);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const u32x4 bs = u32x4{pw[4 * jj], pw[4 * jj + 1], pw[4 * jj + 2], pw[4 * jj + 3]};
-          dq0 = mfma(dq0, ld16(Kt + lq * kPitch + 16 * (2 * slab + jj) + 8 * hf), bs);
-          dq1 = mfma(dq1, ld16(Kt + (32 + lq) * kPitch + 16 * (2 * slab + jj) + 8 * hf), bs);
-        }
-      }
-    }
+    if (!kCausal || k0 <= q_wave0 + 31)  // uniform over the wavefront
+      tile(k0, smem + (t & 1) * 3 * kTileElems, std::true_type());
     if (more) lstore((t + 1) & 1);
     __syncthreads();
   }
@@ -346,81 +367,100 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16(BwdArgs a, float c,
     }
   };
 
+  // One 64-query tile. Keys past a padded length are zeroed at the store, and
+  // queries past n_q have lse = +inf (weight 0), so only tiles that straddle
+  // the causal diagonal mask pairs.
+  auto tile = [&](int q0, int buf, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
+    const bf16* Qs = smem + buf * 4 * kTileElems;
+    const bf16* Qt = Qs + kTileElems;
+    const bf16* Ds = Qs + 2 * kTileElems;
+    const bf16* Dt = Qs + 3 * kTileElems;
+#pragma unroll
+    for (int slab = 0; slab < 2; ++slab) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        s = mfma(s, ld16(Qs + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf), kf[kk]);
+        dp = mfma(dp, ld16(Ds + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf), vf[kk]);
+      }
+      // lse and delta of this lane's 16 queries: two runs of 8
+      float lq16[16], dq16[16];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int base = 32 * slab + 16 * half + 8 * hf;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&s_lse[buf][base]);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&s_lse[buf][base + 4]);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&s_delta[buf][base]);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&s_delta[buf][base + 4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lq16[8 * half + i] = l0[i];
+          lq16[8 * half + 4 + i] = l1[i];
+          dq16[8 * half + i] = d0[i];
+          dq16[8 * half + 4 + i] = d1[i];
+        }
+      }
+      unsigned pp[8], pd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float p2[2], d2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * i + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lq16[r]));
+          if (kMasked) p = my_k <= q0 + 32 * slab + acc_row(r, hf) ? p : 0.f;
+          p2[e] = p;
+          d2[e] = p * (dp[r] - dq16[r]);
+        }
+        pp[i] = pack_bf16(p2[0], p2[1]);
+        pd[i] = pack_bf16(d2[0], d2[1]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x4 bp = u32x4{pp[4 * jj], pp[4 * jj + 1], pp[4 * jj + 2], pp[4 * jj + 3]};
+        const u32x4 bd = u32x4{pd[4 * jj], pd[4 * jj + 1], pd[4 * jj + 2], pd[4 * jj + 3]};
+        const int col = 16 * (2 * slab + jj) + 8 * hf;
+        dv0 = mfma(dv0, ld16(Dt + lq * kPitch + col), bp);
+        dv1 = mfma(dv1, ld16(Dt + (32 + lq) * kPitch + col), bp);
+        dk0 = mfma(dk0, ld16(Qt + lq * kPitch + col), bd);
+        dk1 = mfma(dk1, ld16(Qt + (32 + lq) * kPitch + col), bd);
+      }
+    }
+  };
+
   if (n_tiles > 0) {
     gload(q_begin);
     lstore(0);
   }
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
+  // causal: the first two query tiles straddle the block's diagonal; from the
+  // third on every query lies at or past every key of the block
+  const int t_masked = kCausal ? min(n_tiles, 128 / kBlk) : 0;
+  int t = 0;
+  for (; t < t_masked; ++t) {
     const int q0 = q_begin + t * kBlk;
     const bool more = t + 1 < n_tiles;
     if (more) gload(q0 + kBlk);
-    const int buf = t & 1;
-    const bf16* Qs = smem + buf * 4 * kTileElems;
-    const bf16* Qt = Qs + kTileElems;
-    const bf16* Ds = Qs + 2 * kTileElems;
-    const bf16* Dt = Qs + 3 * kTileElems;
-    if (!kCausal || q0 + kBlk - 1 >= k_wave0) {  // uniform over the wavefront
-#pragma unroll
-      for (int slab = 0; slab < 2; ++slab) {
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          s = mfma(s, ld16(Qs + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf), kf[kk]);
-          dp = mfma(dp, ld16(Ds + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf), vf[kk]);
-        }
-        // lse and delta of this lane's 16 queries: two runs of 8
-        float lq16[16], dq16[16];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int base = 32 * slab + 16 * half + 8 * hf;
-          const f32x4 l0 = *reinterpret_cast<const f32x4*>(&s_lse[buf][base]);
-          const f32x4 l1 = *reinterpret_cast<const f32x4*>(&s_lse[buf][base + 4]);
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&s_delta[buf][base]);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&s_delta[buf][base + 4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            lq16[8 * half + i] = l0[i];
-            lq16[8 * half + 4 + i] = l1[i];
-            dq16[8 * half + i] = d0[i];
-            dq16[8 * half + 4 + i] = d1[i];
-          }
-        }
-        unsigned pp[8], pd[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float p2[2], d2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * i + e;
-            const int qi = q0 + 32 * slab + acc_row(r, hf);
-            const bool vis = key_ok && (!kCausal || my_k <= qi);
-            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lq16[r])) : 0.f;
-            p2[e] = p;
-            d2[e] = p * (dp[r] - dq16[r]);
-          }
-          pp[i] = pack_bf16(p2[0], p2[1]);
-          pd[i] = pack_bf16(d2[0], d2[1]);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const u32x4 bp = u32x4{pp[4 * jj], pp[4 * jj + 1], pp[4 * jj + 2], pp[4 * jj + 3]};
-          const u32x4 bd = u32x4{pd[4 * jj], pd[4 * jj + 1], pd[4 * jj + 2], pd[4 * jj + 3]};
-          const int col = 16 * (2 * slab + jj) + 8 * hf;
-          dv0 = mfma(dv0, ld16(Dt + lq * kPitch + col), bp);
-          dv1 = mfma(dv1, ld16(Dt + (32 + lq) * kPitch + col), bp);
-          dk0 = mfma(dk0, ld16(Qt + lq * kPitch + col), bd);
-          dk1 = mfma(dk1, ld16(Qt + (32 + lq) * kPitch + col), bd);
-        }
-      }
-    }
+    if (q0 + kBlk - 1 >= k_wave0) tile(q0, t & 1, std::true_type());  // uniform over the wavefront
     if (more) lstore((t + 1) & 1);
     __syncthreads();
   }
+  for (; t < n_tiles; ++t) {
+    const int q0 = q_begin + t * kBlk;
+    const bool more = t + 1 < n_tiles;
+    if (more) gload(q0 + kBlk);
+    tile(q0, t & 1, std::false_type());
+    if (more) lstore((t + 1) & 1);
+    __syncthreads();
+  }
+  // keys past a padded length were never masked above (their K and V rows
+  // are zero): they store exactly zero, selected, not multiplied, since
+  // their unmasked weights can overflow
   const bool store_ok = my_k < a.n_k;
   const int out_row = min(my_k, a.n_k - 1);
-  store_rows(dvp + (int64_t)out_row * a.dv_s[2], store_ok, dv0, dv1, 1.0f, hf);
-  store_rows(dkp + (int64_t)out_row * a.dk_s[2], store_ok, dk0, dk1, a.scale, hf);
+  store_rows(dvp + (int64_t)out_row * a.dv_s[2], store_ok, dv0, dv1, 1.0f, hf, !key_ok);
+  store_rows(dkp + (int64_t)out_row * a.dk_s[2], store_ok, dk0, dk1, a.scale, hf, !key_ok);
 }
 
 }  // namespace
