@@ -75,18 +75,85 @@ def torch_tensor(stored, dev):
     return t.to(dev)
 
 
-def time_events(fn, iters, stream):
-    """Average milliseconds per call, HIP events on `stream` around `iters` calls."""
+def time_events(fn, iters, stream, per_step=None):
+    """Average milliseconds per call, HIP events on `stream` around `iters` calls.
+    per_step: optional list that receives each call's own duration (ms), from
+    an event recorded after every call (events do not synchronise)."""
     import torch
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
+    events[0].record(stream)
     for i in range(iters):
         fn(i)
-    end.record(stream)
+        events[i + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / iters
+    if per_step is not None:
+        per_step.extend(events[i].elapsed_time(events[i + 1]) for i in range(iters))
+    return events[0].elapsed_time(events[-1]) / iters
+
+
+def sample_sclk(fn, stream, seconds=0.5):
+    """The shader clock the GPU sustains while `fn` runs back to back: amdsmi
+    readings from a side thread over a separate (untimed) pass. None where
+    amdsmi cannot see this device."""
+    import statistics
+    import threading
+    import torch
+    try:
+        import amdsmi
+        props = torch.cuda.get_device_properties(0)
+        want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        handle = None
+        for h in amdsmi.amdsmi_get_processor_handles():
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
+            dom, bus, rest = bdf.split(":")
+            if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                handle = h
+        if handle is None:
+            return None
+        samples, stop = [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                try:
+                    samples.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.SYS)["clk"])
+                except Exception:
+                    pass
+                time.sleep(0.005)
+        # keep the queue full (no synchronisation while launching) so the GPU
+        # never idles; samples start once the first launches have run
+        for i in range(4):
+            fn(i)
+        torch.cuda.synchronize()
+        th = threading.Thread(target=poll)
+        t0, i = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            fn(i)
+            i += 1
+            if i == 16:
+                th.start()
+        if not th.is_alive():
+            th.start()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        busy = [x for x in samples if isinstance(x, (int, float))]
+        if not busy:
+            return None
+        return {"median_mhz": statistics.median(busy), "min_mhz": min(busy), "max_mhz": max(busy),
+                "samples": len(busy),
+                "how": "amdsmi SYS clock every ~5 ms while the step is launched back to back (separate untimed pass)"}
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def traffic_for(kernel_key, launch_desc):
@@ -350,7 +417,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
     # single process on one GPU: the barrier is the device synchronisation itself
-    ms = time_events(step, args.steps, stream)
+    step_ms = []
+    ms = time_events(step, args.steps, stream, per_step=step_ms)
     value = flops_step / (ms * 1e-3) / 1e12
     log(f"step {ms * 1e3:.1f} us, {value:.1f} TFLOP/s")
 
@@ -395,7 +463,8 @@ def main():
         lms = time_events(fl, 20, stream)
         lt = wl.attention_flops() / (lms * 1e-3) / 1e12
         secondary = {"workload": wl.name, "kernel": "attn_fwd_bf16_d64", "us": round(lms * 1e3, 1),
-                     "tflops": round(lt, 1), "frac_of_peak": round(lt / PEAK_BF16_TFLOPS, 4)}
+                     "tflops": round(lt, 1), "frac_of_peak": round(lt / PEAK_BF16_TFLOPS, 4),
+                     "sclk": sample_sclk(fl, stream)}
         log(f"long causal attention: {lms * 1e3:.1f} us, {lt:.1f} TFLOP/s")
 
     if args.calib_copy:
@@ -405,6 +474,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("calibration copy: 3 x 256 MiB")
+
+    sclk = sample_sclk(step, stream)
+    if sclk:
+        log(f"sustained shader clock: median {sclk['median_mhz']} MHz over {sclk['samples']} samples")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -449,7 +522,9 @@ def main():
             "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg,
-            "pct_of_peak": round(100 * value / peak, 2), "roofline": roofline, "cpu_baseline": cpu}
+            "pct_of_peak": round(100 * value / peak, 2), "roofline": roofline, "cpu_baseline": cpu,
+            "step_ms_median": round(float(np.median(step_ms)), 5), "step_ms_min": round(float(np.min(step_ms)), 5),
+            "sclk": sclk}
     if secondary:
         line["long_causal"] = secondary
     line.update(result)
