@@ -190,6 +190,29 @@ def test_scale_values(dev, scale, dtype):
         assert_close(to_f64(o), want, dtype, f"scale {scale}")
 
 
+@pytest.mark.parametrize("scale", [1.0, 2.0, -1.5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_moves_in_long_query_runs(dev, scale, causal):
+    """Large scales spread the scores over many binary orders, so a row's running
+    reference maximum moves inside a key tile, also on its second 32-key slab.
+    N = 2048 (a multiple of 256 rows) takes the kernel form with 64 query rows per
+    wavefront, which checks both slabs of a tile before their P V products: the
+    weights already computed against the old reference must reach O before O is
+    rescaled. (Found wrong in that form, max-abs error 58 at scale 2.)"""
+    import torch
+    n = 2048
+    q = workloads.random_tensor((1, 2, n, 64), "bf16", seed=61)
+    k = workloads.random_tensor((1, 2, n, 64), "bf16", seed=62)
+    v = workloads.random_tensor((1, 2, n, 64), "bf16", seed=63)
+    say(f"reference moves n={n} scale={scale} causal={causal}")
+    o, lse = mha.attention_forward(to_device(q, dev), to_device(k, dev), to_device(v, dev), causal=causal,
+                                   scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    want, _, want_lse = oracle.attention_ref(q.value, k.value, v.value, causal=causal, scale=scale)
+    assert_close(to_f64(o), want, "bf16", f"scale {scale} causal {causal}")
+    assert max_abs(to_f64(lse), want_lse) <= LSE_TOL["bf16"], "log-sum-exp"
+
+
 # ---------------------------------------------------------------- properties on GPU outputs
 def test_deterministic(dev):
     import torch

@@ -126,14 +126,22 @@ __device__ __forceinline__ void slab_weights(const float (&sv)[16], unsigned (&p
   }
 }
 
+struct NoPending {
+  __device__ void operator()() const {}
+};
+
 // Every weight is <= 2^8 while the reference holds. A weight above 2^8 (or
 // an overflow) makes the lane's 16-weight sum exceed 2^8, so one compare per
 // slab detects when the reference must move; only then is the row maximum
 // formed, O and l rescaled and the slab's weights recomputed. This branch is
 // taken on the first tile and rarely after.
-template <bool kMasked>
+// `flush_pending` adds into O the weights of an earlier slab that were
+// computed against the current reference but not yet multiplied by V; it
+// runs before a move, so that O is rescaled together with them (l already
+// holds their sum).
+template <bool kMasked, typename Pending = NoPending>
 __device__ __forceinline__ void check_reference(RowState& st, const float (&sv)[16], unsigned (&pw)[8], float& ps,
-                                                float c) {
+                                                float c, Pending&& flush_pending = Pending{}) {
   const bool bad = !(ps <= kMaxSlabSum) || st.m == -INFINITY;
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
     asm volatile("" ::: "memory");  // keep a real branch, not predicated code
@@ -142,6 +150,7 @@ __device__ __forceinline__ void check_reference(RowState& st, const float (&sv)[
     for (int r = 1; r < 16; ++r) tmax = __builtin_fmaxf(tmax, sv[r]);
     tmax = max_halves(tmax);
     const float m_new = __builtin_fmaxf(st.m, tmax);
+    if (__builtin_amdgcn_ballot_w64(m_new > st.m) != 0) flush_pending();
     if (m_new > st.m) {
       const float mc_new = m_new * c;
       const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.mc - mc_new);
@@ -192,7 +201,9 @@ __device__ __forceinline__ void mask_slab(float (&sv)[16], const f32x16& s, int 
 //            an eighth of A's softmax; A's eight P V MFMAs each followed by an
 //            eighth of B's softmax; B's P V MFMAs.
 // A reference move (rare) rescales that block's O and l after its earlier
-// P V products, so every term matches the reference it was computed against.
+// P V products, so every term matches the reference it was computed against:
+// with kQB = 2 both slabs of a block are checked before its P V products, so
+// a move found on slab 1 first adds slab 0's weights into O.
 // kMasked (diagonal and ragged-end tiles) runs in plain program order.
 template <bool kMasked, int kQB>
 __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&qf)[kQB][4], const bf16* Ks,
@@ -289,6 +300,20 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
     float sva[2][16], svb[2][16];
     unsigned pwa[2][8], pwb[2][8];
     float psa[2] = {0.f, 0.f}, psb[2] = {0.f, 0.f};
+    // slab 0's weights of a block, added into O (and cleared) ahead of a
+    // reference move found on its slab 1
+    auto pending_a = [&] {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pv_one(st[A], vf[0][j >> 1][j & 1], pwa[0], j >> 1, j & 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pwa[0][j] = 0u;
+    };
+    auto pending_b = [&] {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pv_one(st[B], vf[0][j >> 1][j & 1], pwb[0], j >> 1, j & 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pwb[0][j] = 0u;
+    };
     // B's S^T, each MFMA followed by a quarter slab of A's softmax
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -301,7 +326,12 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
       }
       slab_weights<false>(sva[slab], pwa[slab], psa[slab], st[A].mc, c, 2 * kk, 2 * kk + 2);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk == 3) check_reference<false>(st[A], sva[slab], pwa[slab], psa[slab], c);
+      if (kk == 3) {
+        if (slab == 0)
+          check_reference<false>(st[A], sva[0], pwa[0], psa[0], c);
+        else
+          check_reference<false>(st[A], sva[1], pwa[1], psa[1], c, pending_a);
+      }
     }
     // A's P V, each MFMA followed by a quarter slab of B's softmax
 #pragma unroll
@@ -315,7 +345,12 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
       }
       slab_weights<false>(svb[slab], pwb[slab], psb[slab], st[B].mc, c, 2 * q4, 2 * q4 + 2);
       __builtin_amdgcn_sched_barrier(0);
-      if (q4 == 3) check_reference<false>(st[B], svb[slab], pwb[slab], psb[slab], c);
+      if (q4 == 3) {
+        if (slab == 0)
+          check_reference<false>(st[B], svb[0], pwb[0], psb[0], c);
+        else
+          check_reference<false>(st[B], svb[1], pwb[1], psb[1], c, pending_b);
+      }
     }
     // B's P V
 #pragma unroll
