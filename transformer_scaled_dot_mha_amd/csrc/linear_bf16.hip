@@ -2,39 +2,44 @@
 //
 // The Q, K, V projections and the output projection W^O of multi-head
 // attention ("The Transformer" (hoshank.vercel.app), "The Mathematics",
-// MultiHead equation: each W is a d_model x d_k block applied on the right).
+// MultiHead equation: each W is a d_model x d_k block applied on the right),
+// and the two FFN products of the encoder layer (same page, FFN equation).
 // X is (m, k) row-major, W is (k, n) row-major (in, out), Y is (m, n) row-major.
 // Because head i owns columns [i*d, (i+1)*d), the row-major Y already *is* the
 // head-split (batch, n, heads, d) layout; no permutation pass is needed.
 //
-// Tile 256 x 128 per workgroup of 4 wavefronts (128 x 128 for launches too
-// small to give every CU two workgroups); wavefront w owns rows
-// 64*w .. +63 and all 128 columns as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16,
-// so every fragment read from LDS feeds two or four MFMAs (0.75 KB of LDS
-// reads per MFMA; a 64 x 64 wavefront tile would need 1 KB, the LDS's whole
-// rate at full MFMA issue). The MFMA computes Y^T blocks: its A operand is a
-// 32 x 16 slice of W^T, its B operand a 16 x 32 slice of X^T, and each lane
-// ends with 4 consecutive columns of one row.
-// X and W are staged through LDS in 32-deep k chunks, double buffered (60 KB),
-// with the next chunk's global loads in flight during the MFMAs; two
-// workgroups share a CU, so one computes while the other waits on its loads.
-// X rows are copied as they are (coalesced 16-byte loads, 80-byte LDS rows for
-// conflict-free fragment reads); W is read row-major and transposed while it
-// is written (two k values per column, 4 bytes), so every fragment is one
-// 16-byte read.
-// Raw buffer loads bound every read: rows past m, k past the last column and
-// rows of W past k read as zero, with no per-lane bounds branches.
+// Tile kTM x 128 per workgroup of 4 wavefronts: kTM = 256 (wavefront w owns
+// rows 64w..+63 and all 128 columns, 2 x 4 blocks of v_mfma_f32_32x32x16_bf16)
+// or kTM = 128 (wavefronts 2 x 2, each 64 x 64). The MFMA computes Y^T
+// blocks: its A operand is a 32 x 16 slice of W^T, its B operand a 16 x 32
+// slice of X^T, and each lane ends with 4 consecutive columns of one row.
+//
+// Staging: 32-deep k chunks go straight from global memory into LDS with
+// buffer loads that write LDS (no staging registers, no VALU), into a ring of
+// three stages, two chunks ahead of the one being multiplied; one barrier per
+// chunk. The loads are issued from inline asm and awaited with explicit vmcnt
+// waits, so that the compiler does not wait for every outstanding chunk before
+// each LDS read. X rows keep their layout (64-byte rows, the 16-byte chunk c
+// of row r stored at position c ^ ((r >> 2) & 3), so that the 16-byte
+// fragment reads of 16 consecutive rows hit distinct banks); W rows keep
+// theirs (256-byte rows, chunk c of k-row r at c ^ (r & 15)) and the W^T
+// fragments are read with the transposing LDS load ds_read_b64_tr_b16.
+// Buffer records bound every read: rows past m and rows of W past k read as
+// zero, and so do X chunks past the last column (out-of-range offset).
+//
 // Up to three independent problems sharing n and k run in one launch (the Q,
 // K and V projections); the workgroup order puts the column tiles and groups
 // of one row tile on one XCD, so that a self-attention X row tile is fetched
-// from HBM once.
+// from HBM once. The tile height is the one whose workgroup count fills whole
+// rounds of 512 workgroups (two per CU) best, 128 on ties: at these sizes the
+// kernel is bound by load latency rather than by the matrix cores, and the
+// smaller tile keeps more workgroups in flight.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
 
 namespace mha {
 namespace {
-
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -42,20 +47,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kTN = 128, kTK = 32;
-constexpr int kPitch = 40;  // LDS row pitch in elements (80 bytes: conflict-free 16-byte reads)
-constexpr int kWTile = kTN * kPitch;
-constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family: 32-bit data format)
+constexpr int kXRow = kTK * 2;  // 64-byte X rows in LDS (one k chunk of an m row)
+constexpr int kWRow = kTN * 2;  // 256-byte W rows in LDS (the tile's n columns of a k row)
+constexpr int kNStages = 3;     // LDS ring: chunk c is read while c + 1 and c + 2 load
+constexpr int kBufferFlags = 0x00020000;       // raw buffer descriptor word 3 (gfx9 family: 32-bit data format)
 constexpr unsigned kOutOfRange = 0x80000000u;  // byte offset past any record count: the load returns zero
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   f32x2 f = {lo, hi};
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
-}
-__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 // Pack a lane's 4 values of column group g (columns 8g + 4hf + 0..3) of both
 // lane halves into one 16-byte row chunk: half 0 ends with group 2t, half 1
@@ -65,19 +70,35 @@ __device__ __forceinline__ u32x4 gather_row_chunk(unsigned a0, unsigned a1, unsi
   const auto x1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
   return u32x4{(unsigned)x0[0], (unsigned)x1[0], (unsigned)x0[1], (unsigned)x1[1]};
 }
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ unsigned lds_off(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+// 16 bytes per lane from a raw buffer into LDS at lds_byte + 16 * lane (m0
+// holds the wave-uniform LDS base); offsets past the record write zeros.
+__device__ __forceinline__ void dma16(u32x4 rsrc, unsigned voff, unsigned lds_byte) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_byte)
+               : "memory");
+}
+// Raw buffer descriptor (stride 0) over `bytes` bytes from base.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  return u32x4{(unsigned)b, (unsigned)(b >> 32) & 0xffffu, bytes, (unsigned)kBufferFlags};
+}
 
-// kTM = 256: wavefront w owns rows 64w..+63 and all 128 columns (4 x 2 MFMA
-// blocks). kTM = 128, for launches too small to give every CU two
-// workgroups: wavefronts form 2 x 2, each 64 rows x 64 columns (2 x 2 blocks).
+// kTM = 256: wavefront w owns rows 64w..+63 and all 128 columns (2 x 4 MFMA
+// blocks). kTM = 128: wavefronts form 2 x 2, each 64 rows x 64 columns.
+// LDS stage: X tile (kTM rows x 64 B), then W tile (32 k-rows x 256 B).
 template <int kTM>
 __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, int tiles_n, int tiles_m) {
   constexpr int kWM = kTM / 64;         // wavefronts along m
   constexpr int kWC = 128 / (4 / kWM);  // columns per wavefront
   constexpr int kNB = kWC / 32;         // 32-column MFMA blocks per wavefront
-  constexpr int kXLoads = kTM / 64;     // 16-byte X loads per thread per chunk
-  constexpr int kXTile = kTM * kPitch;
-  constexpr int kStage = kXTile + kWTile;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * kStage];
+  constexpr int kXBytes = kTM * kXRow;
+  constexpr int kStageBytes = kXBytes + kTK * kWRow;
+  constexpr int kXDma = kTM / 64;  // X loads per wavefront per chunk (16 rows of 64 B each)
+  constexpr int kWDma = 2;         // W loads per wavefront per chunk (4 rows of 256 B each)
+  __shared__ __attribute__((aligned(16))) char smem[kNStages * kStageBytes];
   const int n = args.n, kdim = args.k, groups = args.groups;
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; each XCD
@@ -95,80 +116,110 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hf = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wrow = 64 * (wave % kWM), wcol = kWC * (wave / kWM);
   const bf16* X = static_cast<const bf16*>(g.x) + (int64_t)m0 * g.ldx;
   const bf16* W = static_cast<const bf16*>(g.w) + n0;
   bf16* Y = static_cast<bf16*>(g.y);
   const int valid_m = min(kTM, g.m - m0);
   const int valid_n = min(kTN, n - n0);
+  const int ldx = (int)g.ldx, ldw = (int)g.ldw;
 
-  // X staging: 16-byte chunk tid%4 of rows tid/4 + 64*i
-  const int x_c = tid & 3, x_r = tid >> 2;
-  // W staging: k rows 2*(tid%16) + 0..1, 8-column chunk tid/16
-  const int w_q = tid & 15, w_c = tid >> 4;
-  const unsigned w_off = (unsigned)(((int64_t)(2 * w_q) * g.ldw + 8 * w_c) * 2);
-
-  u32x4 xr[kXLoads], wr[2];
-  auto gload = [&](int k0) {
+  const unsigned smem_base = lds_off(smem);
+  // Per-lane load offsets, the same for every chunk (the chunk moves the buffer
+  // base). Load i of wavefront w fills X rows (kTM/4) w + 16 i + 0..15, lane l
+  // LDS position (row l/4, slot l%4), which holds chunk (l%4) ^ ((row >> 2) & 3);
+  // W load i fills k-rows 8w + 4i + 0..3, lane l slot l%16 of row l/16, which
+  // holds chunk (l%16) ^ (row & 15).
+  unsigned xdo[kXDma], wdo[kWDma];
+  int xch[kXDma];
+#pragma unroll
+  for (int i = 0; i < kXDma; ++i) {
+    const int row = (kTM / 4) * wave + 16 * i + (lane >> 2);
+    xch[i] = (lane & 3) ^ ((row >> 2) & 3);
+    xdo[i] = (unsigned)((row * ldx + 8 * xch[i]) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < kWDma; ++i) {
+    const int kr = 8 * wave + 4 * i + (lane >> 4);
+    wdo[i] = (unsigned)((kr * ldw + 8 * ((lane & 15) ^ (kr & 15))) * 2);
+  }
+  // loads of k chunk c into stage c % 3 (X chunks past the last column read zero)
+  auto dma_chunk = [&](int c) {
+    const int k0 = c * kTK;
     const int cols = min(kTK, kdim - k0);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(X + k0), (short)0, (int)(((int64_t)(valid_m - 1) * g.ldx + cols) * 2), kBufferFlags);
-    // k past the last column would read the next row's values: force zero
-    const unsigned xo = 8 * x_c < cols ? (unsigned)(((int64_t)x_r * g.ldx + 8 * x_c) * 2) : kOutOfRange;
-    const unsigned xstep = (unsigned)(64 * g.ldx * 2);
+    const u32x4 rx = make_rsrc(X + k0, (unsigned)(((valid_m - 1) * ldx + cols) * 2));
+    const u32x4 rw = make_rsrc(W + (int64_t)k0 * ldw, (unsigned)(((cols - 1) * ldw + valid_n) * 2));
+    const unsigned sb = smem_base + (unsigned)((c % kNStages) * kStageBytes);
+    const bool full = cols == kTK;  // workgroup-uniform
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i) xr[i] = bload(rx, xo == kOutOfRange ? kOutOfRange : xo + i * xstep);
-    const int rows = min(kTK, kdim - k0);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(W + (int64_t)k0 * g.ldw), (short)0, (int)(((int64_t)(rows - 1) * g.ldw + valid_n) * 2), kBufferFlags);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) wr[i] = bload(rw, w_off + (unsigned)(i * g.ldw * 2));
-  };
-  auto lstore = [&](int buf) {
-    bf16* Xs = smem + buf * kStage;
-    bf16* Wt = Xs + kXTile;
-#pragma unroll
-    for (int i = 0; i < kXLoads; ++i) *reinterpret_cast<u32x4*>(Xs + (x_r + 64 * i) * kPitch + 8 * x_c) = xr[i];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      *reinterpret_cast<unsigned*>(Wt + (8 * w_c + e) * kPitch + 2 * w_q) =
-          __builtin_amdgcn_perm(wr[1][e >> 1], wr[0][e >> 1], sel);
+    for (int i = 0; i < kXDma; ++i) {
+      const unsigned off = (full || 8 * xch[i] < cols) ? xdo[i] : kOutOfRange;
+      dma16(rx, off, sb + (unsigned)(((kTM / 4) * wave_u + 16 * i) * kXRow));
     }
+#pragma unroll
+    for (int i = 0; i < kWDma; ++i) dma16(rw, wdo[i], sb + (unsigned)(kXBytes + (8 * wave_u + 4 * i) * kWRow));
   };
+  // Per-lane fragment offsets within a stage. X (B operand, k step s): row
+  // wrow + 32 mb + lq, chunk 2s + hf. W^T (A operand) through two transposing
+  // reads: in each 16-lane group gi (lane j), read r addresses k-row
+  // 16 s + 8 (gi >> 1) + 4 r + j / 4, columns 32 nb + 16 (gi & 1) + 4 (j % 4) + 0..3,
+  // so lane l receives 4 consecutive k of column 32 nb + l % 32; with the
+  // swizzle the position's bit 2 is (nb & 1) ^ r and bit 3 (nb >> 1) ^ (gi >> 1).
+  unsigned xoff[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) xoff[s] = (unsigned)((wrow + lq) * kXRow + 16 * ((2 * s + hf) ^ ((lq >> 2) & 3)));
+  unsigned woff[2];
+  {
+    const int gi = lane >> 4, j = lane & 15;
+    const int c_lane = 2 * (gi & 1) + ((j & 3) >> 1);
+    const int kr_lane = 8 * (gi >> 1) + (j >> 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)  // h = nb >> 1
+      woff[h] = (unsigned)(kXBytes + kr_lane * kWRow + 16 * (c_lane ^ (j >> 2)) + 8 * (j & 1) + 128 * (h ^ (gi >> 1)));
+  }
 
   f32x16 acc[kNB][2] = {};  // [n block][m block], Y^T layout
-  auto compute = [&](int buf) {
-    const bf16* Xs = smem + buf * kStage;
-    const bf16* Wt = Xs + kXTile;
+  auto compute = [&](int c) {
+    const unsigned sb = smem_base + (unsigned)((c % kNStages) * kStageBytes);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 xf[2], wf[kNB];
+      const lds_char* xp = (const lds_char*)(size_t)(sb + xoff[s]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        xf[mb] = *reinterpret_cast<const u32x4*>(Xs + (wrow + 32 * mb + lq) * kPitch + 16 * s + 8 * hf);
+      for (int mb = 0; mb < 2; ++mb) xf[mb] = *(const __attribute__((address_space(3))) u32x4*)(xp + 32 * mb * kXRow);
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-        wf[nb] = *reinterpret_cast<const u32x4*>(Wt + (wcol + 32 * nb + lq) * kPitch + 16 * s + 8 * hf);
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int col_nb = wcol / 32 + nb;  // 32-column block within the tile
+        const lds_char* wp = (const lds_char*)(size_t)(sb + woff[col_nb >> 1]);
+        const v4i16 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(wp + 16 * s * kWRow + 64 * (col_nb & 1)));
+        const v4i16 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(wp + 16 * s * kWRow + 4 * kWRow + 64 * ((col_nb & 1) ^ 1)));
+        const u32x2 a0 = __builtin_bit_cast(u32x2, w0), a1 = __builtin_bit_cast(u32x2, w1);
+        wf[nb] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+      }
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wf[nb]), as_bf16x8(xf[mb]), acc[nb][mb],
-                                                                0, 0, 0);
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wf[nb]), as_bf16x8(xf[mb]), acc[nb][mb], 0, 0, 0);
     }
   };
 
+  // Chunk c: wait for its loads (the next chunk's may stay in flight), barrier
+  // (which also ends every read of the stage chunk c + 2 reuses), start the
+  // loads of chunk c + 2, multiply.
   const int nchunks = (kdim + kTK - 1) / kTK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  dma_chunk(0);
+  if (nchunks > 1) dma_chunk(1);
   for (int c = 0; c < nchunks; ++c) {
-    const bool more = c + 1 < nchunks;
-    if (more) gload((c + 1) * kTK);
-    compute(c & 1);
-    if (more) lstore((c + 1) & 1);
-    __syncthreads();
+    if (c + 1 < nchunks)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kXDma + kWDma) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + 2 < nchunks) dma_chunk(c + 2);
+    compute(c);
   }
 
   // lane holds row wrow + 32*mb + lq and columns wcol + 32*nb + 8*q + 4*hf + 0..3;
@@ -214,16 +265,18 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
     }
   }
 }
-
 }  // namespace
 
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream) {
   int max_m = 0;
   for (int i = 0; i < a.groups; ++i) max_m = a.g[i].m > max_m ? a.g[i].m : max_m;
   const int tiles_n = (a.n + kTN - 1) / kTN;
-  // 256-row tiles unless that leaves CUs without a second workgroup (2 per CU on 256 CUs)
+  // the tile height whose workgroup count fills whole rounds of 512 (two per
+  // CU) best; ties go to the 128-row tile
   const int64_t big = (int64_t)tiles_n * ((max_m + 255) / 256) * a.groups;
-  if (big >= 512) {
+  const int64_t small = (int64_t)tiles_n * ((max_m + 127) / 128) * a.groups;
+  auto fill = [](int64_t wgs) { return (double)wgs / (double)(((wgs + 511) / 512) * 512); };
+  if (big >= 512 && fill(big) > fill(small)) {
     const int tiles_m = (max_m + 255) / 256;
     hipLaunchKernelGGL((linear_bf16_kernel<256>), dim3((unsigned)big), dim3(256), 0, stream, a, tiles_n, tiles_m);
   } else {
@@ -233,5 +286,4 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream) {
   }
   return hipGetLastError();
 }
-
 }  // namespace mha

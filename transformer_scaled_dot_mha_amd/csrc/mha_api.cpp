@@ -156,7 +156,7 @@ mha_status validate_linear(const void* x, const void* w, void* y, int m, int n, 
     return fail(MHA_ERR_INVALID_ARG, "x, w and y must be 16-byte aligned");
   const int64_t tiles = (int64_t)((m + 63) / 64) * ((n + 63) / 64);
   if (tiles > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
-  // the bf16 kernel addresses a 256-row slice of X and a 64-row slice of W
+  // the bf16 kernel addresses a 256-row slice of X and a 32-row slice of W
   // with 32-bit byte offsets
   if (ldx > kMaxLdX || ldw > kMaxLdW)
     return fail(MHA_ERR_UNSUPPORTED, "leading dimension too large (ldx=%lld, at most %lld; ldw=%lld, at most %lld)",
