@@ -42,6 +42,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 F
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 HBM_GBPS = 8000.0
 ROTATE_BYTES = 512 << 20    # > 2x the 256 MB Infinity Cache
+LEAD_SECONDS = 0.2          # back-to-back launches ahead of each timed pass
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "attention": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_bf16.hip"),
@@ -75,85 +76,118 @@ def torch_tensor(stored, dev):
     return t.to(dev)
 
 
-def time_events(fn, iters, stream, per_step=None):
+def time_events(fn, iters, stream, per_step=None, lead_in=0, lead_seconds=0.0):
     """Average milliseconds per call, HIP events on `stream` around `iters` calls.
+
+    Before the first event the stream is synchronised and then fed, without
+    a host wait, `lead_in` calls, or as many as take `lead_seconds` on the GPU
+    (from one call timed beforehand) if that is more: the timed calls continue
+    a stream that is already running.
+    (After a pause of a few milliseconds the clock dips for the next tens of
+    launches -- the long causal launch went from 285 to 354 us and back -- so
+    a timed pass that starts from an idle GPU would measure that transient.)
     per_step: optional list that receives each call's own duration (ms), from
-    an event recorded after every call (events do not synchronise)."""
+    an event recorded after every call. Recording an event between launches
+    leaves a gap of several microseconds on the stream, so a per-call pass is
+    kept apart from the timed one (without per_step only the two bracketing
+    events are recorded)."""
     import torch
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    n_ev = iters + 1 if per_step is not None else 2
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    if lead_seconds > 0:
+        # size the lead-in from one call's duration (the host enqueues far faster
+        # than the GPU runs, so a host-time bound would queue seconds of work)
+        torch.cuda.synchronize()
+        events[0].record(stream)
+        fn(0)
+        events[-1].record(stream)
+        torch.cuda.synchronize()
+        one_s = max(events[0].elapsed_time(events[-1]) * 1e-3, 1e-6)
+        lead_in = max(lead_in, int(math.ceil(lead_seconds / one_s)))
     torch.cuda.synchronize()
+    for j in range(lead_in):
+        fn(j)
+    j = lead_in
     events[0].record(stream)
     for i in range(iters):
-        fn(i)
-        events[i + 1].record(stream)
+        fn(j + i)
+        if per_step is not None:
+            events[i + 1].record(stream)
+    if per_step is None:
+        events[1].record(stream)
     torch.cuda.synchronize()
     if per_step is not None:
         per_step.extend(events[i].elapsed_time(events[i + 1]) for i in range(iters))
     return events[0].elapsed_time(events[-1]) / iters
 
 
+def back_to_back(fn, seconds, start_hook=None):
+    """Launch fn back to back (no synchronisation while launching) for about
+    `seconds` of host time, then wait for the queue to drain. start_hook runs
+    once the first launches are queued."""
+    import torch
+    for i in range(4):
+        fn(i)
+    torch.cuda.synchronize()
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i == 16 and start_hook is not None:
+            start_hook()
+            start_hook = None
+    if start_hook is not None:
+        start_hook()
+    torch.cuda.synchronize()
+
+
 def sample_sclk(fn, stream, seconds=0.5):
-    """The shader clock the GPU sustains while `fn` runs back to back: amdsmi
-    readings from a side thread over a separate (untimed) pass. None where
-    amdsmi cannot see this device."""
+    """Run fn back to back for `seconds` (a separate, untimed pass) and return
+    the shader clock the GPU sustains meanwhile: amdsmi readings from a side
+    thread. None where amdsmi cannot see this device."""
     import statistics
     import threading
     import torch
+    handle, amdsmi = None, None
     try:
         import amdsmi
         props = torch.cuda.get_device_properties(0)
         want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
         amdsmi.amdsmi_init()
-    except Exception:
-        return None
-    try:
-        handle = None
         for h in amdsmi.amdsmi_get_processor_handles():
             bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
             dom, bus, rest = bdf.split(":")
             if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
                 handle = h
-        if handle is None:
-            return None
-        samples, stop = [], threading.Event()
-
-        def poll():
-            while not stop.is_set():
-                try:
-                    samples.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.SYS)["clk"])
-                except Exception:
-                    pass
-                time.sleep(0.005)
-        # keep the queue full (no synchronisation while launching) so the GPU
-        # never idles; samples start once the first launches have run
-        for i in range(4):
-            fn(i)
-        torch.cuda.synchronize()
-        th = threading.Thread(target=poll)
-        t0, i = time.perf_counter(), 0
-        while time.perf_counter() - t0 < seconds:
-            fn(i)
-            i += 1
-            if i == 16:
-                th.start()
-        if not th.is_alive():
-            th.start()
-        torch.cuda.synchronize()
-        stop.set()
-        th.join()
-        busy = [x for x in samples if isinstance(x, (int, float))]
-        if not busy:
-            return None
-        return {"median_mhz": statistics.median(busy), "min_mhz": min(busy), "max_mhz": max(busy),
-                "samples": len(busy),
-                "how": "amdsmi SYS clock every ~5 ms while the step is launched back to back (separate untimed pass)"}
     except Exception:
-        return None
+        handle = None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                samples.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.SYS)["clk"])
+            except Exception:
+                pass
+            time.sleep(0.005)
+    th = threading.Thread(target=poll) if handle is not None else None
+    try:
+        back_to_back(fn, seconds, th.start if th is not None else None)
     finally:
-        try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:
-            pass
+        if th is not None:
+            stop.set()
+            th.join()
+        if amdsmi is not None:
+            try:
+                amdsmi.amdsmi_shut_down()
+            except Exception:
+                pass
+    busy = [x for x in samples if isinstance(x, (int, float))]
+    if not busy:
+        return None
+    return {"median_mhz": statistics.median(busy), "min_mhz": min(busy), "max_mhz": max(busy),
+            "samples": len(busy),
+            "how": "amdsmi SYS clock every ~5 ms while the step is launched back to back (separate untimed pass)"}
 
 
 def traffic_for(kernel_key, launch_desc):
@@ -413,19 +447,21 @@ def main():
         get_out = lambda: outs[0]
 
     log(f"warmup {args.warmup}, timing {args.steps} steps ({n_sets} rotating input sets)")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # single process on one GPU: the barrier is the device synchronisation itself
+    # single process on one GPU: the barrier is the device synchronisation itself.
+    # The W warm-up steps close a 0.2 s lead-in of back-to-back steps, and the
+    # timed steps follow them on the running stream.
+    ms = time_events(step, args.steps, stream, lead_in=args.warmup, lead_seconds=LEAD_SECONDS)
+    # per-step statistics from a second, untimed pass with an event after every step
     step_ms = []
-    ms = time_events(step, args.steps, stream, per_step=step_ms)
+    time_events(step, args.steps, stream, per_step=step_ms, lead_in=args.warmup, lead_seconds=LEAD_SECONDS)
     value = flops_step / (ms * 1e-3) / 1e12
     log(f"step {ms * 1e3:.1f} us, {value:.1f} TFLOP/s")
 
     # attention-only workloads: the timed step is the one attention launch, so its
     # average duration is the step time itself; an MHA step re-times its attention
     # launch alone on the same workspace views
-    dom_ms = ms if dom_fn is step else time_events(dom_fn, max(args.steps, 20), stream)
+    dom_ms = ms if dom_fn is step else time_events(dom_fn, max(args.steps, 20), stream, lead_in=3,
+                                                   lead_seconds=LEAD_SECONDS)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     launch_desc = f"{dom_name}:{w.name}"
@@ -458,9 +494,7 @@ def main():
         ql, kl, vl = (torch_tensor(xl[n], dev) for n in ("q", "k", "v"))
         ol = torch.empty_like(ql)
         fl = lambda i: mha.attention_forward(ql, kl, vl, causal=True, out=ol)
-        for i in range(3):
-            fl(i)
-        lms = time_events(fl, 20, stream)
+        lms = time_events(fl, 20, stream, lead_in=3, lead_seconds=LEAD_SECONDS)
         lt = wl.attention_flops() / (lms * 1e-3) / 1e12
         secondary = {"workload": wl.name, "kernel": "attn_fwd_bf16_d64", "us": round(lms * 1e3, 1),
                      "tflops": round(lt, 1), "frac_of_peak": round(lt / PEAK_BF16_TFLOPS, 4),
