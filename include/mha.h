@@ -263,7 +263,9 @@ mha_status encoder_layer_forward(const void* x, const mha_encoder_weights* weigh
  * causal, scale, kv_len: as in attention_forward_padded (kv_len may be NULL).
  *   Keys at or past kv_len[b] get dK = dV = 0.
  * workspace: DEVICE scratch of at least attention_backward_workspace_size()
- *   bytes (delta, fp32 per query row), 16-byte aligned.
+ *   bytes (two fp32 values per query row, written by the first launch and
+ *   read by the second: delta, and for bf16 the row's lse times log2(e)),
+ *   16-byte aligned.
  * Supported: as attention_forward (bf16: d = 64; f32: d in {16, 32, 64, 128}).
  * bf16: P and dS are rounded to bf16 for the matrix products (as P is in the
  *   forward), every accumulation is fp32, and dq, dk, dv are rounded once.

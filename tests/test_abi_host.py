@@ -321,5 +321,5 @@ def test_backward_validation(lib, kw, status, needle):
 
 
 def test_backward_workspace_size(lib):
-    assert lib.attention_backward_workspace_size(2, 8, 100) == (2 * 8 * 100 * 4 + 255) // 256 * 256
+    assert lib.attention_backward_workspace_size(2, 8, 100) == (2 * 8 * 100 * 8 + 255) // 256 * 256
     assert lib.attention_backward_workspace_size(0, 8, 100) == 0

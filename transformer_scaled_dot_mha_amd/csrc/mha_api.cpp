@@ -460,7 +460,8 @@ mha_status backward_impl(const void* q, const void* k, const void* v, const void
   }
   if (!aligned16(lse) || !aligned16(workspace)) return fail(MHA_ERR_INVALID_ARG, "lse and workspace must be 16-byte aligned");
   if (kv_len && !aligned4(kv_len)) return fail(MHA_ERR_INVALID_ARG, "kv_len must be 4-byte aligned");
-  const size_t need = round_up((size_t)batch * heads * n_q * 4);
+  // two fp32 rows per query: -delta and lse log2(e) (the fp32 path uses the first for delta)
+  const size_t need = round_up((size_t)batch * heads * n_q * 8);
   if (workspace_bytes < need)
     return fail(MHA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
   const int64_t kblocks = (int64_t)batch * heads * ((n_k + 63) / 64);
@@ -500,7 +501,7 @@ const char* mha_status_string(mha_status s) {
 
 const char* mha_last_error(void) { return g_last_error.c_str(); }
 
-int mha_version(void) { return 400; }
+int mha_version(void) { return 401; }
 
 mha_status attention_forward(const void* q, const void* k, const void* v, void* o, int batch, int heads,
                              int n_q, int n_k, int d_k, int d_v, const int64_t q_strides[3],
@@ -619,7 +620,7 @@ mha_status attention_decode(const void* q, const mha_kv_cache* cache, const int3
 
 size_t attention_backward_workspace_size(int batch, int heads, int n_q) {
   if (batch < 1 || heads < 1 || n_q < 1) return 0;
-  const unsigned __int128 bytes = (unsigned __int128)batch * heads * n_q * 4;
+  const unsigned __int128 bytes = (unsigned __int128)batch * heads * n_q * 8;
   if (bytes > ((unsigned __int128)1 << 62)) return 0;
   return round_up((size_t)bytes);
 }
