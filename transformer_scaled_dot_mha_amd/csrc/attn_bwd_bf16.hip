@@ -37,16 +37,17 @@
 //
 // Staging: the streamed tiles go from global memory straight into LDS with
 // buffer loads that write LDS, into a ring of four stages (each a 64-row tile
-// of both streamed matrices); a tile is loaded three tiles ahead of its use,
-// and one wait plus barrier per tile makes the next tile visible. Rows keep
+// of both streamed matrices); the loads of tile t + 3 are issued while tile t
+// is processed (about two tiles of work before they are first read), and one
+// wait plus barrier per tile makes the next tile visible. Rows keep
 // their 128-byte layout with the 16-byte chunk c of row r at c ^ swz(r), so
 // that both the row reads and the transposing reads hit distinct banks.
 //
 // Schedule: a wavefront's work is a sequence of units u, each a 32-row slab
 // of a tile against its own 32 rows: A(u) (the S and dP products), V(u) (the
 // per-element exponent and dS, VALU) and B(u) (the gradient products). VALU
-// work issued right after a matrix-core instruction of the same wavefront
-// overlaps it, so iteration u runs the products B(u-1) and A(u+1) with the
+// work issued right after a matrix-core instruction of the same wavefront can
+// overlap it, so iteration u runs the products B(u-1) and A(u+1) with the
 // element steps of V(u) spread between them, and the three steps of each
 // element (x = s c - lse2; p = exp2(x); dS = p (dP - delta), pack) are
 // staggered so that consecutive instructions do not wait on each other.
