@@ -185,6 +185,16 @@ __device__ __forceinline__ void mask_slab(float (&sv)[16], const f32x16& s, int 
 #pragma unroll
   for (int r = 0; r < 16; ++r) sv[r] = 32 * slab + 16 * (r >> 3) + (r & 7) <= last ? s[r] : -INFINITY;
 }
+// The slab's scores for the softmax: masked on diagonal and ragged-end tiles.
+template <bool kMasked>
+__device__ __forceinline__ void scores_of_impl(float (&sv)[16], const f32x16& s, int slab, int last) {
+  if (kMasked) {
+    mask_slab(sv, s, slab, last);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = s[r];
+  }
+}
 
 // One 64-key tile for one wavefront holding kQB blocks of 32 query rows.
 // Each block's tile is two 32-key slabs (register r of a slab holds key
@@ -204,41 +214,19 @@ __device__ __forceinline__ void mask_slab(float (&sv)[16], const f32x16& s, int 
 // P V products, so every term matches the reference it was computed against:
 // with kQB = 2 both slabs of a block are checked before its P V products, so
 // a move found on slab 1 first adds slab 0's weights into O.
-// kMasked (diagonal and ragged-end tiles) runs in plain program order.
+// kMasked (diagonal and ragged-end tiles) runs the same order, with masked
+// keys' scores set to -inf before the softmax.
 template <bool kMasked, int kQB>
 __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&qf)[kQB][4], const bf16* Ks,
                                             const bf16* Vt, const int (&last)[kQB], int lq, int hf, float c) {
+  auto scores_of = [&](float (&sv)[16], const f32x16& s, int slab, int lst) {
+    scores_of_impl<kMasked>(sv, s, slab, lst);
+  };
   u32x4 kf[2][4];
 #pragma unroll
   for (int slab = 0; slab < 2; ++slab)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) kf[slab][kk] = ld16(Ks + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf);
-
-  if (kMasked) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      f32x16 s[2] = {};
-#pragma unroll
-      for (int slab = 0; slab < 2; ++slab)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) s[slab] = qk_one(s[slab], kf[slab][kk], qf[qb][kk]);
-#pragma unroll
-      for (int slab = 0; slab < 2; ++slab) {
-        float sv[16];
-        unsigned pw[8];
-        float ps = 0.f;
-        mask_slab(sv, s[slab], slab, last[qb]);
-        slab_weights<true>(sv, pw, ps, st[qb].mc, c, 0, 8);
-        check_reference<true>(st[qb], sv, pw, ps, c);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int blk = 0; blk < 2; ++blk)
-            pv_one(st[qb], ld16(Vt + (32 * blk + lq) * kPitch + 16 * (2 * slab + jj) + 8 * hf), pw, jj, blk);
-      }
-    }
-    return;
-  }
 
   if (kQB == 1) {
     u32x4 vf0[2][2];
@@ -256,29 +244,25 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
     for (int kk = 0; kk < 4; ++kk) {
       s1 = qk_one(s1, kf[1][kk], qf[0][kk]);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv0[r] = s0[r];
-      }
-      slab_weights<false>(sv0, pw0, ps0, st[0].mc, c, 2 * kk, 2 * kk + 2);
+      if (kk == 0) scores_of(sv0, s0, 0, last[0]);
+      slab_weights<kMasked>(sv0, pw0, ps0, st[0].mc, c, 2 * kk, 2 * kk + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    check_reference<false>(st[0], sv0, pw0, ps0, c);
+    check_reference<kMasked>(st[0], sv0, pw0, ps0, c);
     u32x4 vf1[2][2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) vf1[jj][blk] = ld16(Vt + (32 * blk + lq) * kPitch + 16 * (2 + jj) + 8 * hf);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sv1[r] = s1[r];
+    scores_of(sv1, s1, 1, last[0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pv_one(st[0], vf0[i >> 1][i & 1], pw0, i >> 1, i & 1);
       __builtin_amdgcn_sched_barrier(0);
-      slab_weights<false>(sv1, pw1, ps1, st[0].mc, c, 2 * i, 2 * i + 2);
+      slab_weights<kMasked>(sv1, pw1, ps1, st[0].mc, c, 2 * i, 2 * i + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    check_reference<false>(st[0], sv1, pw1, ps1, c);
+    check_reference<kMasked>(st[0], sv1, pw1, ps1, c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv_one(st[0], vf1[i >> 1][i & 1], pw1, i >> 1, i & 1);
   } else {
@@ -320,17 +304,14 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
       const int slab = i >> 2, kk = i & 3;
       sb[slab] = qk_one(sb[slab], kf[slab][kk], qf[B][kk]);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sva[slab][r] = sa[slab][r];
-      }
-      slab_weights<false>(sva[slab], pwa[slab], psa[slab], st[A].mc, c, 2 * kk, 2 * kk + 2);
+      if (kk == 0) scores_of(sva[slab], sa[slab], slab, last[A]);
+      slab_weights<kMasked>(sva[slab], pwa[slab], psa[slab], st[A].mc, c, 2 * kk, 2 * kk + 2);
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 3) {
         if (slab == 0)
-          check_reference<false>(st[A], sva[0], pwa[0], psa[0], c);
+          check_reference<kMasked>(st[A], sva[0], pwa[0], psa[0], c);
         else
-          check_reference<false>(st[A], sva[1], pwa[1], psa[1], c, pending_a);
+          check_reference<kMasked>(st[A], sva[1], pwa[1], psa[1], c, pending_a);
       }
     }
     // A's P V, each MFMA followed by a quarter slab of B's softmax
@@ -339,17 +320,14 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
       const int slab = i >> 2, jj = (i >> 1) & 1, blk = i & 1, q4 = i & 3;
       pv_one(st[A], vf[slab][jj][blk], pwa[slab], jj, blk);
       __builtin_amdgcn_sched_barrier(0);
-      if (q4 == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) svb[slab][r] = sb[slab][r];
-      }
-      slab_weights<false>(svb[slab], pwb[slab], psb[slab], st[B].mc, c, 2 * q4, 2 * q4 + 2);
+      if (q4 == 0) scores_of(svb[slab], sb[slab], slab, last[B]);
+      slab_weights<kMasked>(svb[slab], pwb[slab], psb[slab], st[B].mc, c, 2 * q4, 2 * q4 + 2);
       __builtin_amdgcn_sched_barrier(0);
       if (q4 == 3) {
         if (slab == 0)
-          check_reference<false>(st[B], svb[0], pwb[0], psb[0], c);
+          check_reference<kMasked>(st[B], svb[0], pwb[0], psb[0], c);
         else
-          check_reference<false>(st[B], svb[1], pwb[1], psb[1], c, pending_b);
+          check_reference<kMasked>(st[B], svb[1], pwb[1], psb[1], c, pending_b);
       }
     }
     // B's P V
