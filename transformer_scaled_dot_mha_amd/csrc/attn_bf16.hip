@@ -166,6 +166,20 @@ __device__ __forceinline__ void check_reference(RowState& st, const float (&sv)[
   st.l += ps;
 }
 
+// The reference of a block that has seen no key yet (O = 0, l = 0), from the
+// row maximum of its first slab's scores: those weights are then <= 1 and the
+// check after them passes without recomputing them.
+__device__ __forceinline__ void first_reference(RowState& st, const float (&sv)[16], float c) {
+  float tmax = sv[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) tmax = __builtin_fmaxf(tmax, sv[r]);
+  tmax = max_halves(tmax);
+  if (tmax > st.m) {
+    st.m = tmax;
+    st.mc = tmax * c;
+  }
+}
+
 // One P V MFMA: 16 keys (step jj of a slab) into d block blk of O^T.
 __device__ __forceinline__ void pv_one(RowState& st, const u32x4& vfrag, const unsigned (&pw)[8], int jj, int blk) {
   const bf16x8 bp = as_bf16x8(u32x4{pw[4 * jj], pw[4 * jj + 1], pw[4 * jj + 2], pw[4 * jj + 3]});
@@ -216,11 +230,14 @@ __device__ __forceinline__ void scores_of_impl(float (&sv)[16], const f32x16& s,
 // a move found on slab 1 first adds slab 0's weights into O.
 // kMasked (diagonal and ragged-end tiles) runs the same order, with masked
 // keys' scores set to -inf before the softmax.
-template <bool kMasked, int kQB>
+template <bool kMasked, int kQB, bool kFirst = false>
 __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&qf)[kQB][4], const bf16* Ks,
                                             const bf16* Vt, const int (&last)[kQB], int lq, int hf, float c) {
-  auto scores_of = [&](float (&sv)[16], const f32x16& s, int slab, int lst) {
+  // the slab's scores; on a wavefront's first (unmasked) tile, slab 0 also
+  // sets its block's reference, so that its weights need no second pass
+  auto scores_of = [&](float (&sv)[16], const f32x16& s, int slab, int lst, RowState& rs) {
     scores_of_impl<kMasked>(sv, s, slab, lst);
+    if (kFirst && slab == 0) first_reference(rs, sv, c);
   };
   u32x4 kf[2][4];
 #pragma unroll
@@ -244,7 +261,7 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
     for (int kk = 0; kk < 4; ++kk) {
       s1 = qk_one(s1, kf[1][kk], qf[0][kk]);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) scores_of(sv0, s0, 0, last[0]);
+      if (kk == 0) scores_of(sv0, s0, 0, last[0], st[0]);
       slab_weights<kMasked>(sv0, pw0, ps0, st[0].mc, c, 2 * kk, 2 * kk + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -254,7 +271,7 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) vf1[jj][blk] = ld16(Vt + (32 * blk + lq) * kPitch + 16 * (2 + jj) + 8 * hf);
-    scores_of(sv1, s1, 1, last[0]);
+    scores_of(sv1, s1, 1, last[0], st[0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pv_one(st[0], vf0[i >> 1][i & 1], pw0, i >> 1, i & 1);
@@ -304,7 +321,7 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
       const int slab = i >> 2, kk = i & 3;
       sb[slab] = qk_one(sb[slab], kf[slab][kk], qf[B][kk]);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) scores_of(sva[slab], sa[slab], slab, last[A]);
+      if (kk == 0) scores_of(sva[slab], sa[slab], slab, last[A], st[A]);
       slab_weights<kMasked>(sva[slab], pwa[slab], psa[slab], st[A].mc, c, 2 * kk, 2 * kk + 2);
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 3) {
@@ -320,7 +337,7 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
       const int slab = i >> 2, jj = (i >> 1) & 1, blk = i & 1, q4 = i & 3;
       pv_one(st[A], vf[slab][jj][blk], pwa[slab], jj, blk);
       __builtin_amdgcn_sched_barrier(0);
-      if (q4 == 0) scores_of(svb[slab], sb[slab], slab, last[B]);
+      if (q4 == 0) scores_of(svb[slab], sb[slab], slab, last[B], st[B]);
       slab_weights<kMasked>(svb[slab], pwb[slab], psb[slab], st[B].mc, c, 2 * q4, 2 * q4 + 2);
       __builtin_amdgcn_sched_barrier(0);
       if (q4 == 3) {
@@ -464,6 +481,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
   const int t_split = min(kCausal ? qblk * (kRows / kBN) : ntiles, n_k / kBN);
   const int no_mask[kQB] = {};
   int t = 0;
+  if (t_split > 0) {  // the first tile sets each block's reference from its first slab
+    const bool more = 1 < ntiles;
+    if (more) gload(kBN);
+    attend_tile<false, kQB, true>(st, qf, smem, smem + kTile, no_mask, lq, hf, c);
+    if (more) lstore(1);
+    __syncthreads();
+    t = 1;
+  }
   for (; t < t_split; ++t) {
     const bool more = t + 1 < ntiles;
     if (more) gload((t + 1) * kBN);
