@@ -31,9 +31,10 @@
 // K and V projections); the workgroup order puts the column tiles and groups
 // of one row tile on one XCD, so that a self-attention X row tile is fetched
 // from HBM once. The tile height is the one whose workgroup count fills whole
-// rounds of 512 workgroups (two per CU) best, 128 on ties: at these sizes the
-// kernel is bound by load latency rather than by the matrix cores, and the
-// smaller tile keeps more workgroups in flight.
+// rounds of 512 workgroups best, 128 on ties: at these sizes the kernel is
+// bound by load latency rather than by the matrix cores, and the smaller tile
+// keeps more workgroups in flight (three per CU against two for the 256-row
+// tile, by LDS).
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -271,8 +272,9 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream) {
   int max_m = 0;
   for (int i = 0; i < a.groups; ++i) max_m = a.g[i].m > max_m ? a.g[i].m : max_m;
   const int tiles_n = (a.n + kTN - 1) / kTN;
-  // the tile height whose workgroup count fills whole rounds of 512 (two per
-  // CU) best; ties go to the 128-row tile
+  // the tile height whose workgroup count fills whole rounds of 512 best (the
+  // 256-row tile's residency, two per CU; the 128-row tile, 48 KB of LDS,
+  // fits three); ties go to the 128-row tile
   const int64_t big = (int64_t)tiles_n * ((max_m + 255) / 256) * a.groups;
   const int64_t small = (int64_t)tiles_n * ((max_m + 127) / 128) * a.groups;
   auto fill = [](int64_t wgs) { return (double)wgs / (double)(((wgs + 511) / 512) * 512); };
