@@ -121,6 +121,12 @@ EDGE = [
     (1, 2, 3000, 3000, True, "bf16"),
     (1, 1, 2500, 2600, False, "bf16"),
     (1, 1, 4100, 4100, True, "bf16"),
+    # unmasked query runs that fill whole 256-row workgroups also take 64 rows per wavefront;
+    # ragged key counts on either side of a key tile, and 640 rows (which stays at 32)
+    (2, 2, 512, 300, False, "bf16"),
+    (1, 3, 768, 769, False, "bf16"),
+    (1, 1, 1024, 64, False, "bf16"),
+    (1, 2, 640, 640, False, "bf16"),
     (1, 1, 1, 1, True, "f32"),
     (2, 3, 65, 65, True, "f32"),
     (1, 2, 100, 37, False, "f32"),
