@@ -17,8 +17,14 @@ Prints ONE JSON line. `value` is algorithmic TFLOP/s of the step (FLOPs =
 4*B*H*d*unmasked pairs for attention, 2*m*n*k per projection) with inputs
 already resident in HBM; input and output buffers rotate over more than twice
 the 256 MB Infinity Cache so each step reads its inputs from HBM.
-`roofline` covers the step's dominant kernel, timed with HIP events on the
-stream it runs on. `cpu_baseline` times the fp64 CPU oracle on the host cores.
+`launches` lists every launch of the step (for the encoder step: the grouped
+Q/K/V projection, the attention, W^O), each re-timed alone on its own rotating
+inputs with HIP events on the stream it runs on; `roofline` belongs to the
+longest of them. The other configurations (the tiny fp32 MHA, the decoder's
+causal attention, cross-attention, the long causal attention) get a line each
+(`tiny_mha`, `decoder_causal`, `cross_attention`, `long_causal`), timed the same
+way. `cpu_baseline` times the fp64 CPU oracle on the host cores; `env` records
+the ROCm and HIP versions and the device.
 """
 from __future__ import annotations
 
@@ -43,6 +49,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 HBM_GBPS = 8000.0
 ROTATE_BYTES = 512 << 20    # > 2x the 256 MB Infinity Cache
 LEAD_SECONDS = 0.2          # back-to-back launches ahead of each timed pass
+SCLK_PLAUSIBLE_MHZ = (500, 2400)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "attention": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_bf16.hip"),
@@ -182,15 +189,19 @@ def sample_sclk(fn, stream, seconds=0.5):
                 amdsmi.amdsmi_shut_down()
             except Exception:
                 pass
-    busy = [x for x in samples if isinstance(x, (int, float))]
+    read = [x for x in samples if isinstance(x, (int, float))]
+    # a busy MI355X runs between a few hundred MHz and its 2400 MHz maximum; a
+    # reading outside that range is a misread of the sensor, not a clock
+    busy = [x for x in read if SCLK_PLAUSIBLE_MHZ[0] <= x <= SCLK_PLAUSIBLE_MHZ[1]]
     if not busy:
         return None
     return {"median_mhz": statistics.median(busy), "min_mhz": min(busy), "max_mhz": max(busy),
-            "samples": len(busy),
-            "how": "amdsmi SYS clock every ~5 ms while the step is launched back to back (separate untimed pass)"}
+            "samples": len(busy), "dropped_implausible": len(read) - len(busy),
+            "how": "amdsmi SYS clock every ~5 ms while the step is launched back to back (separate untimed pass); "
+                   f"readings outside {SCLK_PLAUSIBLE_MHZ[0]}-{SCLK_PLAUSIBLE_MHZ[1]} MHz dropped"}
 
 
-def traffic_for(kernel_key, launch_desc):
+def traffic_for(src_key, launch_desc):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     if that summary is missing or was taken on a different kernel source."""
     try:
@@ -198,9 +209,14 @@ def traffic_for(kernel_key, launch_desc):
             rec = json.load(f).get(launch_desc)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel_key]):
+    if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[src_key]):
         return None
     return rec.get("bytes_per_launch")
+
+
+def src_key_of(kernel):
+    return ("linear" if kernel.startswith("linear") else "decode" if kernel.startswith("decode")
+            else "backward" if kernel.startswith("attn_bwd") else "attention")
 
 
 def cpu_baseline(w, inputs, min_seconds=10.0, max_seconds=30.0):
@@ -263,17 +279,136 @@ def cpu_baseline(w, inputs, min_seconds=10.0, max_seconds=30.0):
             flops = 4 * w.batch * w.heads * w.d_k * pairs
             sample = (f"{len(rows)} sampled query positions x {w.batch * w.heads} (batch, head) pairs, "
                       "each against all visible keys, oracle.attention_ref in float64")
-    runs, t0 = 0, time.perf_counter()
+    # three timed runs, each repeating the sample until a third of min_seconds has
+    # passed (at least once); the median run's rate is reported
+    rates, total_runs, t_all = [], 0, time.perf_counter()
     result = None
-    while True:
-        result = fn()
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or el + el / runs > max_seconds:
+    for _ in range(3):
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            result = fn()
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds / 3 or time.perf_counter() - t_all + el / runs > max_seconds:
+                break
+        rates.append(flops * runs / el / 1e12)
+        total_runs += runs
+        if time.perf_counter() - t_all > max_seconds:
             break
-    return {"value": round(flops * runs / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "sample": f"{sample}; {runs} run(s) in {el:.1f} s",
+    el_all = time.perf_counter() - t_all
+    return {"value": round(float(np.median(rates)), 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{sample}; median of {len(rates)} timed run(s) ({total_runs} evaluations in {el_all:.1f} s)",
+            "runs_tflops": [round(r, 6) for r in rates],
             "host_cpus": os.cpu_count(), "blas": ",".join(sorted({d.get("internal_api", "?") for d in info}))}, result
+
+
+def env_info():
+    """ROCm and HIP versions and the device, for the record."""
+    import subprocess
+    import torch
+    info = {"torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=60).stdout
+        m = re.search(r"HIP version:\s*(\S+)", out)
+        info["hipcc_hip_version"] = m.group(1) if m else None
+        m = re.search(r"clang version\s*(\S+)", out)
+        info["hipcc_clang"] = m.group(1) if m else None
+    except (OSError, subprocess.SubprocessError):
+        info["hipcc_hip_version"] = None
+    p = torch.cuda.get_device_properties(0)
+    info["gpu"] = p.name
+    info["arch"] = getattr(p, "gcnArchName", None)
+    info["compute_units"] = p.multi_processor_count
+    return info
+
+
+def mha_step_launches(mha, w, x, ws, kv_len, lens, dev):
+    """The three launches of one mha_forward step, each callable alone on its own
+    rotating inputs (more than twice the Infinity Cache, so operands come from HBM):
+    the grouped Q/K/V projection (linear_forward_grouped: the launch mha_forward
+    makes), the attention over the head-split views, and W^O (linear_forward).
+    Algorithmic bytes: each operand read once, each result written once."""
+    import torch
+    B, N, Nk, H, d, dm = w.batch, w.n_q, w.n_k, w.heads, w.d_k, w.d_model
+    esz = x.element_size()
+    rq, rk = B * N, B * Nk
+    gen = torch.Generator(device=dev).manual_seed(77)
+    rnd = lambda *shape: torch.randn(shape, device=dev, generator=gen).to(x.dtype)
+    out = []
+
+    # Q/K/V projection: X (shared by the three products of self-attention) and W^Q, W^K, W^V in; Q, K, V out
+    per = (rq * dm + (rq + 2 * rk) * dm) * esz
+    n_q = max(1, math.ceil(ROTATE_BYTES / per))
+    qsets = [(x.view(rq, dm) if i == 0 else rnd(rq, dm),
+              [torch.empty((r, dm), dtype=x.dtype, device=dev) for r in (rq, rk, rk)]) for i in range(n_q)]
+    fq = lambda i: mha.linear_forward_grouped([qsets[i % n_q][0]] * 3, ws[:3], outs=qsets[i % n_q][1])
+    out.append({"launch": "qkv_projection", "kernel": "linear_bf16_kernel", "fn": fq,
+                "flops": 2 * dm * dm * (rq + 2 * rk), "bytes": (rq * dm + 3 * dm * dm + (rq + 2 * rk) * dm) * esz,
+                "sets": n_q})
+
+    # attention over (B, N, H, d) buffers seen as (B, H, N, d): Q, K, V in (K, V over the visible keys), O out
+    kv_rows = rk if lens is None else int(lens.astype(np.int64).sum())
+    per = (2 * rq * dm + 2 * rk * dm) * esz
+    n_a = max(1, math.ceil(ROTATE_BYTES / per))
+    asets = [(rnd(B, N, H, d).transpose(1, 2), rnd(B, Nk, H, d).transpose(1, 2), rnd(B, Nk, H, d).transpose(1, 2),
+              torch.empty((B, N, H, d), dtype=x.dtype, device=dev).transpose(1, 2)) for _ in range(n_a)]
+    fa = lambda i: mha.attention_forward(*asets[i % n_a][:3], causal=w.causal, out=asets[i % n_a][3], kv_len=kv_len)
+    out.append({"launch": "attention", "kernel": "attn_fwd_bf16_d64" if w.dtype == "bf16" else "attn_fwd_f32",
+                "fn": fa, "flops": w.attention_flops(), "bytes": (2 * rq * dm + 2 * H * kv_rows * d) * esz,
+                "sets": n_a})
+
+    # W^O: the concatenated heads (rq, dm) in, out (rq, dm)
+    per = 2 * rq * dm * esz
+    n_o = max(1, math.ceil(ROTATE_BYTES / per))
+    osets = [(rnd(rq, dm), torch.empty((rq, dm), dtype=x.dtype, device=dev)) for _ in range(n_o)]
+    fo = lambda i: mha.linear_forward(osets[i % n_o][0], ws[3], out=osets[i % n_o][1])
+    out.append({"launch": "output_projection", "kernel": "linear_bf16_kernel", "fn": fo,
+                "flops": 2 * rq * dm * dm, "bytes": (2 * rq * dm + dm * dm) * esz, "sets": n_o})
+    return out
+
+
+def time_secondary(mha, name, stream, dev, iters):
+    """One of the other configurations, timed alone on rotating inputs: attention
+    workloads run one attention_forward, the tiny fp32 one a whole mha_forward."""
+    import torch
+    w = workloads.get(name)
+    x = workloads.make_inputs(w)
+    if w.kind == "mha":
+        t = {k: torch_tensor(v, dev) for k, v in x.items()}
+        esz = t["x"].element_size()
+        fn = lambda i: mha.mha_forward(t["x"], t["x"], t["x"], t["wq"], t["wk"], t["wv"], t["wo"], w.heads)
+        flops, n_sets, kernel = w.total_flops(), 1, "mha_forward (3 launches)"
+        nbytes = (2 * t["x"].numel() + 4 * w.d_model * w.d_model) * esz
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    else:
+        q, k, v = (torch_tensor(x[n], dev) for n in ("q", "k", "v"))
+        nbytes = (2 * q.numel() + k.numel() + v.numel()) * q.element_size()
+        n_sets = max(1, math.ceil(ROTATE_BYTES / nbytes))
+        sets = [(q, k, v)] + [(q.clone(), k.clone(), v.clone()) for _ in range(n_sets - 1)]
+        outs = [torch.empty_like(q) for _ in range(n_sets)]
+        fn = lambda i: mha.attention_forward(*sets[i % n_sets], causal=w.causal, out=outs[i % n_sets])
+        flops, peak, kernel = w.attention_flops(), PEAK_BF16_TFLOPS, "attn_fwd_bf16_d64"
+    fn(0)
+    torch.cuda.synchronize()
+    ms = time_events(fn, iters, stream, lead_in=3, lead_seconds=LEAD_SECONDS)
+    tf = flops / (ms * 1e-3) / 1e12
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    rec = {"workload": w.name, "kernel": kernel, "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
+           "frac_of_peak": round(tf / peak, 4), "peak": peak, "algorithmic_bytes": nbytes, "gbps": round(gbps, 1),
+           "frac_of_hbm": round(gbps / HBM_GBPS, 4), "rotating_sets": n_sets,
+           "traffic": traffic_for("attention", f"attention:{w.name}") if w.kind == "attn" else None}
+    log(f"{w.name}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f} % of peak), {gbps:.0f} GB/s")
+    return rec, fn, w
+
+
+# the configurations besides the timed workload, each on one line of its own in the record
+SECONDARY = {"tiny": "tiny_mha", "decoder": "decoder_causal", "cross": "cross_attention", "long": "long_causal"}
 
 
 def main():
@@ -284,7 +419,7 @@ def main():
     ap.add_argument("--workload", default="encoder",
                     help="encoder | tiny | decoder | cross | long | padded | layer | decode | bwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true", help="skip the long causal attention line")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other configurations' lines")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -309,6 +444,8 @@ def main():
     result = {}
     lens = w.kv_lengths()
     kv_len = None if lens is None else torch.from_numpy(lens).to(dev)
+    # `launches`: the kernels of the step, each with a callable that runs it alone
+    # (the step itself where the step is one launch or one fused pair of launches)
     if w.kind == "bwd":
         q, k, v, do = (torch_tensor(inputs[n], dev) for n in ("q", "k", "v", "do"))
         # the forward's output and log-sum-exp, saved once as training saves them
@@ -330,8 +467,8 @@ def main():
         torch.cuda.synchronize()
         flops_step = w.backward_flops()
         # the step is the backward itself: the dQ launch, then the dK/dV launch
-        dom_fn, dom_flops, dom_name = step, flops_step, "attn_bwd_dq_bf16+attn_bwd_dkdv_bf16"
-        dom_bytes = per_set
+        launches = [{"launch": "backward", "kernel": "attn_bwd_dq_bf16+attn_bwd_dkdv_bf16", "fn": step,
+                     "flops": flops_step, "bytes": per_set, "sets": n_sets}]
         get_out = lambda: grads[0]
     elif w.kind == "decode":
         table_np, num_pages = w.pages()
@@ -358,10 +495,12 @@ def main():
         step(0)
         torch.cuda.synchronize()
         flops_step = w.attention_flops()
-        # the step is the decode itself: the split kernel and the merge of the splits
-        dom_fn, dom_flops, dom_name = step, flops_step, "decode_split_kernel+decode_merge_kernel"
+        # the step is the decode itself: the split kernel and the merge of the splits;
         # algorithmic bytes: every visible cached key and value row, q in, o out
-        dom_bytes = (2 * w.heads * int(lens.astype(np.int64).sum()) * w.d_k + 2 * w.batch * w.heads * w.d_k) * esz
+        launches = [{"launch": "decode", "kernel": "decode_split_kernel+decode_merge_kernel", "fn": step,
+                     "flops": flops_step, "sets": n_sets,
+                     "bytes": (2 * w.heads * int(lens.astype(np.int64).sum()) * w.d_k
+                               + 2 * w.batch * w.heads * w.d_k) * esz}]
         get_out = lambda: outs[0]
     elif w.kind == "layer":
         dm, ff = w.d_model, w.d_ff
@@ -381,15 +520,14 @@ def main():
         step(0)
         torch.cuda.synchronize()
         flops_step = w.total_flops()
-        # dominant kernel: the FFN's first product (rows x d_model by d_model x d_ff, the largest
-        # launch of the layer), re-timed alone on workspace-sized buffers; same kernel, same grid
+        # the FFN's first product (rows x d_model by d_model x d_ff, the longest launch of the
+        # layer by the kernel trace), re-timed alone on rotating workspace-sized buffers
         rows = w.batch * w.n_q
-        h_in = torch.empty((rows, dm), dtype=x.dtype, device=dev).copy_(x.view(rows, dm))
-        hid = torch.empty((rows, ff), dtype=x.dtype, device=dev)
-        dom_fn = lambda i: mha.linear_forward(h_in, params["w1"], out=hid)
-        dom_flops = 2 * rows * dm * ff
-        dom_name = "linear_bf16_kernel"
-        dom_bytes = (rows * dm + dm * ff + rows * ff) * x.element_size()
+        nf = max(1, math.ceil(ROTATE_BYTES / ((rows * dm + rows * ff) * x.element_size())))
+        fsets = [(x.view(rows, dm).clone(), torch.empty((rows, ff), dtype=x.dtype, device=dev)) for _ in range(nf)]
+        launches = [{"launch": "ffn_w1", "kernel": "linear_bf16_kernel", "sets": nf,
+                     "fn": lambda i: mha.linear_forward(fsets[i % nf][0], params["w1"], out=fsets[i % nf][1]),
+                     "flops": 2 * rows * dm * ff, "bytes": (rows * dm + dm * ff + rows * ff) * x.element_size()}]
         get_out = lambda: outs[0]
     elif w.kind == "mha":
         dm = w.d_model
@@ -412,21 +550,7 @@ def main():
         step(0)
         torch.cuda.synchronize()
         flops_step = w.total_flops()
-        # dominant kernel: the attention launch inside mha_forward, re-timed alone on the
-        # same workspace views (same kernel, same grid)
-        B, N, H, d = w.batch, w.n_q, w.heads, w.d_k
-        qv = work[:B * N * dm * esz].view(x.dtype).view(B, N, H, d).transpose(1, 2)
-        off_k = (B * N * dm * esz + 255) // 256 * 256
-        kv = work[off_k:off_k + B * w.n_k * dm * esz].view(x.dtype).view(B, w.n_k, H, d).transpose(1, 2)
-        off_v = off_k + (B * w.n_k * dm * esz + 255) // 256 * 256
-        vv = work[off_v:off_v + B * w.n_k * dm * esz].view(x.dtype).view(B, w.n_k, H, d).transpose(1, 2)
-        ov = torch.empty((B, N, H, d), dtype=x.dtype, device=dev).transpose(1, 2)
-        dom_fn = lambda i: mha.attention_forward(qv, kv, vv, causal=w.causal, out=ov, kv_len=kv_len)
-        dom_flops = w.attention_flops()
-        dom_name = "attn_fwd_bf16_d64" if w.dtype == "bf16" else "attn_fwd_f32"
-        # Q in, O out; K and V only over the visible keys
-        kv_rows = B * w.n_k if lens is None else int(lens.astype(np.int64).sum())
-        dom_bytes = 2 * (B * H * N * d + 2 * H * kv_rows * d + B * H * N * d) * (esz // 2)
+        launches = mha_step_launches(mha, w, xs[0], ws, kv_len, lens, dev)
         get_out = lambda: outs[0]
     else:
         q, k, v = (torch_tensor(inputs[n], dev) for n in ("q", "k", "v"))
@@ -442,8 +566,8 @@ def main():
         step(0)
         torch.cuda.synchronize()
         flops_step = w.attention_flops()
-        dom_fn, dom_flops, dom_name = step, flops_step, "attn_fwd_bf16_d64"
-        dom_bytes = per_set
+        launches = [{"launch": "attention", "kernel": "attn_fwd_bf16_d64" if w.dtype == "bf16" else "attn_fwd_f32",
+                     "fn": step, "flops": flops_step, "bytes": per_set, "sets": n_sets}]
         get_out = lambda: outs[0]
 
     log(f"warmup {args.warmup}, timing {args.steps} steps ({n_sets} rotating input sets)")
@@ -456,50 +580,55 @@ def main():
     time_events(step, args.steps, stream, per_step=step_ms, lead_in=args.warmup, lead_seconds=LEAD_SECONDS)
     value = flops_step / (ms * 1e-3) / 1e12
     log(f"step {ms * 1e3:.1f} us, {value:.1f} TFLOP/s")
-
-    # attention-only workloads: the timed step is the one attention launch, so its
-    # average duration is the step time itself; an MHA step re-times its attention
-    # launch alone on the same workspace views
-    dom_ms = ms if dom_fn is step else time_events(dom_fn, max(args.steps, 20), stream, lead_in=3,
-                                                   lead_seconds=LEAD_SECONDS)
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    launch_desc = f"{dom_name}:{w.name}"
-    src_key = ("linear" if dom_name.startswith("linear") else "decode" if dom_name.startswith("decode")
-               else "backward" if dom_name.startswith("attn_bwd") else "attention")
-    gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
+
+    # each launch of the step: its own average duration (HIP events on the launch
+    # stream around back-to-back launches); where the step is that launch, the step's
+    per_launch = []
+    for L in launches:
+        L_ms = ms if L["fn"] is step else time_events(L["fn"], max(args.steps, 20), stream, lead_in=3,
+                                                      lead_seconds=LEAD_SECONDS)
+        tf = L["flops"] / (L_ms * 1e-3) / 1e12
+        gbps = L["bytes"] / (L_ms * 1e-3) / 1e9
+        traffic = traffic_for(src_key_of(L["kernel"]), f"{L['launch']}:{w.name}")
+        rec = {"launch": L["launch"], "kernel": L["kernel"], "avg_launch_us": round(L_ms * 1e3, 2),
+               "tflops": round(tf, 2), "frac_of_peak": round(tf / peak, 4), "algorithmic_bytes": L["bytes"],
+               "gbps": round(gbps, 1), "traffic": traffic,
+               "traffic_over_algorithmic": None if traffic is None else round(traffic / L["bytes"], 3),
+               "rotating_sets": L["sets"]}
+        per_launch.append(rec)
+        log(f"launch {L['launch']} ({L['kernel']}): {L_ms * 1e3:.1f} us, {tf:.1f} TFLOP/s, {gbps:.0f} GB/s")
+
+    # the roofline belongs to the launch that takes longest
+    dom = max(per_launch, key=lambda r: r["avg_launch_us"])
     if w.kind == "decode":
         # one query row: 2 flops per byte-pair of K/V, far below the MFMA ridge -- HBM-bound
-        roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(gbps, 1), "peak": HBM_GBPS,
-                    "unit": "GB/s", "frac": round(gbps / HBM_GBPS, 4),
-                    "traffic": traffic_for(src_key, launch_desc), "algorithmic_bytes": dom_bytes,
-                    "avg_launch_us": round(dom_ms * 1e3, 2),
-                    "achieved_tflops": round(achieved, 3)}
+        roofline = {"bound": "hbm", "launch": dom["launch"], "kernel": dom["kernel"], "achieved": dom["gbps"],
+                    "peak": HBM_GBPS, "unit": "GB/s", "frac": round(dom["gbps"] / HBM_GBPS, 4),
+                    "traffic": dom["traffic"], "algorithmic_bytes": dom["algorithmic_bytes"],
+                    "avg_launch_us": dom["avg_launch_us"], "achieved_tflops": dom["tflops"]}
     else:
-        roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": traffic_for(src_key, launch_desc),
-                    "algorithmic_bytes": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
-                    "achieved_gbps": round(gbps, 1)}
+        roofline = {"bound": "mfma", "launch": dom["launch"], "kernel": dom["kernel"], "achieved": dom["tflops"],
+                    "peak": peak, "unit": "TFLOP/s", "frac": dom["frac_of_peak"], "traffic": dom["traffic"],
+                    "algorithmic_bytes": dom["algorithmic_bytes"], "avg_launch_us": dom["avg_launch_us"],
+                    "achieved_gbps": dom["gbps"]}
         if w.kind == "bwd":
             # the two launches recompute S and dP to avoid atomics: 7 products per pair, 5 counted
-            roofline["executed_tflops"] = round(achieved * 14 / 10, 2)
+            roofline["executed_tflops"] = round(dom["tflops"] * 14 / 10, 2)
             roofline["launches_per_step"] = 2
-    log(f"dominant kernel {dom_name}: {dom_ms * 1e3:.1f} us, {achieved:.1f} TFLOP/s, {gbps:.0f} GB/s")
+    log(f"dominant launch {dom['launch']} ({dom['kernel']}): {dom['avg_launch_us']} us, frac {roofline['frac']}")
 
-    secondary = None
-    if not args.no_secondary and w.name != workloads.get("long").name:
-        wl = workloads.get("long")
-        xl = workloads.make_inputs(wl)
-        ql, kl, vl = (torch_tensor(xl[n], dev) for n in ("q", "k", "v"))
-        ol = torch.empty_like(ql)
-        fl = lambda i: mha.attention_forward(ql, kl, vl, causal=True, out=ol)
-        lms = time_events(fl, 20, stream, lead_in=3, lead_seconds=LEAD_SECONDS)
-        lt = wl.attention_flops() / (lms * 1e-3) / 1e12
-        secondary = {"workload": wl.name, "kernel": "attn_fwd_bf16_d64", "us": round(lms * 1e3, 1),
-                     "tflops": round(lt, 1), "frac_of_peak": round(lt / PEAK_BF16_TFLOPS, 4),
-                     "sclk": sample_sclk(fl, stream)}
-        log(f"long causal attention: {lms * 1e3:.1f} us, {lt:.1f} TFLOP/s")
+    secondary = {}
+    if not args.no_secondary:
+        for name, key in SECONDARY.items():
+            if workloads.get(name).name == w.name:
+                continue
+            rec, fn, wl = time_secondary(mha, name, stream, dev, 20)
+            if name == "long":
+                rec["sclk"] = sample_sclk(fn, stream)
+            secondary[key] = rec
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
 
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -557,11 +686,12 @@ def main():
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg,
             "pct_of_peak": round(100 * value / peak, 2), "roofline": roofline, "cpu_baseline": cpu,
+            "launches": per_launch,
             "step_ms_median": round(float(np.median(step_ms)), 5), "step_ms_min": round(float(np.min(step_ms)), 5),
             "sclk": sclk}
-    if secondary:
-        line["long_causal"] = secondary
+    line.update(secondary)
     line.update(result)
+    line["env"] = env_info()
     print(json.dumps(line), flush=True)
 
 

@@ -130,6 +130,25 @@ mha_status linear_forward(const void* x, const void* w, void* y, int m, int n, i
                           int64_t ldx, int64_t ldw, int64_t ldy, mha_dtype dtype, void* stream);
 
 /*
+ * linear_forward_grouped -- up to three independent projections Y_g = X_g W_g
+ * that share n and k, in ONE launch: the launch mha_forward makes for the
+ * Q, K and V projections ("The Transformer" (hoshank.vercel.app), "The
+ * Mathematics", MultiHead equation: one d_model x d_k block per head of each
+ * of W^Q, W^K, W^V, applied on the right).
+ *
+ * x, w, y, m, ldx, ldw, ldy: host arrays of `groups` entries (1 <= groups <= 3);
+ *   entry g describes problem g exactly as linear_forward's arguments do
+ *   (x[g] (m[g], k), w[g] (k, n), y[g] (m[g], n), row-major, device pointers
+ *   owned by the caller). The host arrays are read during the call only.
+ * Every rule and status of linear_forward applies to each problem; a groups
+ *   value outside [1, 3] or a NULL array is MHA_ERR_INVALID_ARG.
+ */
+mha_status linear_forward_grouped(const void* const* x, const void* const* w, void* const* y,
+                                  const int* m, int groups, int n, int k, const int64_t* ldx,
+                                  const int64_t* ldw, const int64_t* ldy, mha_dtype dtype,
+                                  void* stream);
+
+/*
  * mha_forward_workspace_size -- bytes of device workspace mha_forward needs:
  * room for the projected Q (batch*n_q x d_model), K and V (batch*n_k x
  * d_model each) and the concatenated head outputs (batch*n_q x d_model), in

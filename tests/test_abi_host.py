@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_boundary():
     fns = header_functions()
     assert {"attention_forward", "attention_forward_padded", "mha_forward", "mha_forward_padded",
-            "mha_forward_workspace_size", "linear_forward", "encoder_layer_workspace_size",
+            "mha_forward_workspace_size", "linear_forward", "linear_forward_grouped", "encoder_layer_workspace_size",
             "encoder_layer_forward", "attention_decode_workspace_size", "attention_decode",
             "attention_backward_workspace_size", "attention_backward",
             "mha_status_string", "mha_last_error", "mha_version"} == set(fns)
@@ -179,6 +179,37 @@ def test_linear_validation(lib, kw, status):
     a.update(kw)
     assert lib.linear_forward(a["x"], a["w"], a["y"], a["m"], a["n"], a["k"], a["ldx"], a["ldw"], a["ldy"],
                               a["dtype"], None) == status
+
+
+def grouped(lib, groups=3, n=64, k=64, dtype=_lib.MHA_BF16, **over):
+    vp = lambda v: (ctypes.c_void_p * 3)(*v)
+    a = dict(x=[FAKE] * 3, w=[FAKE] * 3, y=[FAKE] * 3, m=[64, 64, 64], ldx=[64] * 3, ldw=[64] * 3, ldy=[64] * 3)
+    a.update(over)
+    return lib.linear_forward_grouped(vp(a["x"]), vp(a["w"]), vp(a["y"]), (ctypes.c_int * 3)(*a["m"]), groups, n, k,
+                                      (ctypes.c_int64 * 3)(*a["ldx"]), (ctypes.c_int64 * 3)(*a["ldw"]),
+                                      (ctypes.c_int64 * 3)(*a["ldy"]), dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(groups=0), _lib.MHA_ERR_INVALID_ARG, "groups"),
+    (dict(groups=4), _lib.MHA_ERR_INVALID_ARG, "groups"),
+    (dict(x=[FAKE, FAKE, None]), _lib.MHA_ERR_INVALID_ARG, "non-null"),
+    (dict(m=[64, 0, 64]), _lib.MHA_ERR_INVALID_ARG, "sizes"),
+    (dict(y=[FAKE, MIS, FAKE]), _lib.MHA_ERR_INVALID_ARG, "aligned"),
+    (dict(ldw=[64, 64, 32]), _lib.MHA_ERR_INVALID_ARG, "leading"),
+    (dict(k=12), _lib.MHA_ERR_INVALID_ARG, "multiples"),
+    (dict(dtype=7), _lib.MHA_ERR_INVALID_ARG, "dtype"),
+    (dict(ldx=[64, (1 << 21) + 8, 64]), _lib.MHA_ERR_UNSUPPORTED, "leading dimension too large"),
+])
+def test_linear_grouped_validation(lib, kw, status, needle):
+    assert grouped(lib, **kw) == status
+    assert needle in lib.mha_last_error().decode()
+
+
+def test_linear_grouped_null_arrays(lib):
+    i64 = (ctypes.c_int64 * 3)(64, 64, 64)
+    assert lib.linear_forward_grouped(None, None, None, None, 1, 64, 64, i64, i64, i64, 1, None) == \
+        _lib.MHA_ERR_INVALID_ARG
 
 
 def test_last_error_is_thread_local(lib):

@@ -262,17 +262,59 @@ def test_key_permutation_invariance_on_gpu(dev):
 
 
 # ---------------------------------------------------------------- projections and full MHA variants
-@pytest.mark.parametrize("m,n,k,dtype", [(1, 8, 8, "bf16"), (300, 136, 72, "bf16"), (2048, 512, 512, "bf16"),
-                                         (257, 520, 136, "bf16"), (1000, 1536, 512, "bf16"), (64, 128, 1040, "bf16"),
-                                         (16384, 512, 512, "bf16"), (37, 20, 12, "f32"), (129, 512, 512, "f32")])
+def _linear_tile_rows(m, n, groups=1):
+    """Tile height the bf16 projection launcher picks (its rule restated here
+    so that each case below is known to reach the form it is meant for): the
+    height whose workgroup count fills whole rounds of 512 best, 128 on ties."""
+    tiles_n = (n + 127) // 128
+    big = tiles_n * ((m + 255) // 256) * groups
+    small = tiles_n * ((m + 127) // 128) * groups
+    fill = lambda w: w / (((w + 511) // 512) * 512)
+    return 256 if big >= 512 and fill(big) > fill(small) else 128
+
+
+LINEAR_CASES = [
+    (1, 8, 8, "bf16"), (300, 136, 72, "bf16"), (2048, 512, 512, "bf16"), (257, 520, 136, "bf16"),
+    (1000, 1536, 512, "bf16"), (64, 128, 1040, "bf16"), (16384, 512, 512, "bf16"),
+    # 256-row tiles: 512 workgroups fill whole rounds, with ragged m and a partial last k chunk
+    (8000, 2048, 520, "bf16"), (32513, 512, 512, "bf16"), (32640, 512, 512, "bf16"),
+    (37, 20, 12, "f32"), (129, 512, 512, "f32"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,dtype", LINEAR_CASES)
 def test_linear_parity(dev, m, n, k, dtype):
     import torch
     x = workloads.random_tensor((m, k), dtype, seed=31)
     wt = workloads.random_tensor((k, n), dtype, seed=32, scale=1 / math.sqrt(k))
-    say(f"linear {m}x{k}x{n} {dtype}")
+    say(f"linear {m}x{k}x{n} {dtype} ({_linear_tile_rows(m, n)}-row tiles)")
     y = mha.linear_forward(to_device(x, dev), to_device(wt, dev))
     torch.cuda.synchronize()
     assert_close(to_f64(y), oracle.linear_ref(x.value, wt.value), dtype, "linear")
+
+
+def test_linear_cases_reach_both_tile_heights():
+    """The case list above selects both bf16 tile forms (a host-side check of the list)."""
+    heights = {_linear_tile_rows(m, n) for m, n, k, dt in LINEAR_CASES if dt == "bf16"}
+    assert heights == {128, 256}
+
+
+def test_mha_with_256_row_projection_tiles(dev):
+    """B * N = 16385 rows: the grouped Q/K/V launch takes 256-row tiles (780
+    workgroups fill 76 % of two rounds against 75.6 % for 1548 of 128 rows),
+    W^O takes 128-row tiles; the last row tile holds one row."""
+    import torch
+    B, N, dm, h = 29, 565, 512, 8
+    assert B * N == 16385 and _linear_tile_rows(B * N, dm, groups=3) == 256
+    x = workloads.random_tensor((B, N, dm), "bf16", seed=1301)
+    ws = [workloads.random_tensor((dm, dm), "bf16", seed=1302 + i, scale=1 / math.sqrt(dm)) for i in range(4)]
+    t = to_device(x, dev)
+    say(f"mha_forward {B}x{N} d_model={dm} (256-row Q/K/V tiles)")
+    out = mha.mha_forward(t, t, t, *[to_device(s, dev) for s in ws], h)
+    torch.cuda.synchronize()
+    want = oracle.mha_ref(x.value, x.value, x.value, *[s.value for s in ws], h)
+    err = assert_close(to_f64(out), want, "bf16", "mha 16385 rows")
+    say(f"mha 16385 rows: max-abs {err:.3e}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -329,6 +371,12 @@ PADDED = [
     (3, 2, 129, 129, True, "bf16", [129, 64, 200]),
     (2, 3, 2600, 2600, True, "bf16", [2600, 1000]),
     (2, 1, 2100, 2300, False, "bf16", [0, 2299]),
+    # 64 query rows per wavefront (whole 256-row workgroups) under per-item lengths:
+    # 0, below one slab, not a multiple of 64, full
+    (4, 2, 512, 512, False, "bf16", [512, 300, 37, 0]),
+    (1, 2, 2048, 2048, True, "bf16", [1000]),
+    (2, 2, 2048, 2048, True, "bf16", [2048, 1000]),
+    (3, 1, 768, 1000, False, "bf16", [1000, 63, 513]),
     (3, 2, 70, 90, False, "f32", [90, 33, 0]),
     (2, 2, 65, 65, True, "f32", [65, 7]),
 ]
@@ -407,6 +455,14 @@ ENCODER_CASES = [
     (3, 130, 512, 8, 2048, "bf16", False, [130, 45, 0]),
     (2, 70, 256, 4, 512, "f32", False, [70, 21]),
     (1, 65, 128, 2, 256, "f32", True, None),
+    # rows wider than 512 columns: the LayerNorm wavefront holds 2, 4 or 8 chunks per row.
+    # The big model's width (1024, 16 heads of 64; "The Transformer" (hoshank.vercel.app),
+    # "The Mathematics"), and fp32 widths with 128- and 16-wide heads, one with a partial chunk
+    (2, 130, 1024, 16, 4096, "bf16", False, [130, 77]),
+    (1, 70, 1024, 16, 1024, "bf16", True, None),
+    (1, 40, 2048, 16, 512, "f32", False, None),
+    (1, 33, 1040, 65, 256, "f32", True, None),
+    (1, 24, 4096, 32, 256, "f32", False, [17]),
 ]
 
 
@@ -427,3 +483,41 @@ def test_encoder_layer_parity(dev, B, N, dm, h, ff, dtype, causal, lens):
     bound = ENC_TOL[dtype][0] + ENC_TOL[dtype][1] * np.abs(want)
     say(f"encoder layer max-abs {err.max():.3e}, worst ratio to bound {float((err / bound).max()):.3f}")
     assert np.all(err <= bound), f"max-abs {err.max():.3e}"
+
+
+def test_encoder_layer_workload_parity(dev):
+    """The encoder-layer bench workload at full size (B = 32, N = 512, d_model 512,
+    d_ff 2048, bf16), in the launch configuration the bench times."""
+    import torch
+    w = workloads.get("layer")
+    x = workloads.make_inputs(w)
+    params = {k: to_device(v, dev) for k, v in x.items() if k != "x"}
+    say(f"encoder_layer_forward {w.name}")
+    out = mha.encoder_layer_forward(to_device(x["x"], dev), params, w.heads)
+    torch.cuda.synchronize()
+    want = oracle.encoder_layer_ref(x["x"].value, _oracle_params({k: v for k, v in x.items() if k != "x"}), w.heads)
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - want)
+    bound = ENC_TOL["bf16"][0] + ENC_TOL["bf16"][1] * np.abs(want)
+    say(f"{w.name}: max-abs {err.max():.3e}, worst ratio to bound {float((err / bound).max()):.3f}")
+    assert np.all(err <= bound), f"max-abs {err.max():.3e}"
+
+
+def test_padded_mha_workload_parity(dev):
+    """The padded encoder bench workload at full size (B = 32, N = 512, per-item key
+    lengths in [64, 512]), in the launch configuration the bench times."""
+    import torch
+    w = workloads.get("padded")
+    x = workloads.make_inputs(w)
+    t = {k_: to_device(s, dev) for k_, s in x.items()}
+    lens = w.kv_lengths()
+    kv_len = torch.from_numpy(lens).to(dev)
+    say(f"mha_forward_padded {w.name}")
+    out = mha.mha_forward(t["x"], t["x"], t["x"], t["wq"], t["wk"], t["wv"], t["wo"], w.heads, kv_len=kv_len)
+    torch.cuda.synchronize()
+    xv = x["x"].value
+    want = oracle.mha_ref(xv, xv, xv, x["wq"].value, x["wk"].value, x["wv"].value, x["wo"].value, w.heads,
+                          kv_len=lens)
+    err = assert_close(to_f64(out), want, "bf16", w.name)
+    say(f"{w.name}: max-abs {err:.3e}")

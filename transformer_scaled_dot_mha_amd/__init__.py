@@ -16,7 +16,8 @@ from ._lib import (ENCODER_WEIGHT_NAMES, EncoderWeights, KVCache, MHA_BF16, MHA_
                    MHA_ERR_WORKSPACE, MHA_F32, MHA_OK, LIB_PATH, MHAError, check, load, strides3)
 
 __all__ = ["attention_backward", "attention_backward_workspace_size", "attention_decode",
-           "attention_decode_workspace_size", "attention_forward", "encoder_layer_forward", "encoder_layer_workspace_size", "linear_forward",
+           "attention_decode_workspace_size", "attention_forward", "encoder_layer_forward", "encoder_layer_workspace_size",
+           "linear_forward", "linear_forward_grouped",
            "mha_forward", "mha_forward_workspace_size",
            "MHAError", "MHA_F32", "MHA_BF16", "LIB_PATH", "load"]
 
@@ -206,6 +207,37 @@ def linear_forward(x, w, *, out=None, stream=None):
                                 w.stride(0), out.stride(0), _dtype_code(x), _stream_handle(dev, stream))
     check(st)
     return out
+
+
+def linear_forward_grouped(xs, ws, *, outs=None, stream=None):
+    """Y_g = X_g W_g for up to three problems sharing n and k, in one launch
+    (the launch mha_forward makes for its Q, K and V projections)."""
+    torch = _torch()
+    if not 1 <= len(xs) <= 3 or len(ws) != len(xs):
+        raise ValueError("one to three (x, w) pairs are needed")
+    dev = _require_device(*xs, *ws)
+    k, n = ws[0].shape
+    for x, w in zip(xs, ws):
+        if x.shape[1] != k or tuple(w.shape) != (k, n):
+            raise ValueError("every problem must share n and k")
+        if x.stride(1) != 1 or w.stride(1) != 1:
+            raise ValueError("x and w must be row-major with contiguous rows")
+    if outs is None:
+        outs = [torch.empty((x.shape[0], n), dtype=x.dtype, device=dev) for x in xs]
+    for x, y in zip(xs, outs):
+        _require_device(x, y)
+        if tuple(y.shape) != (x.shape[0], n) or y.stride(1) != 1:
+            raise ValueError("each out must be (m, n) row-major")
+    g = len(xs)
+    ptrs = lambda ts: (ctypes.c_void_p * g)(*[t.data_ptr() for t in ts])
+    lds = lambda ts: (ctypes.c_int64 * g)(*[t.stride(0) for t in ts])
+    lib = load()
+    with _on_device(dev):
+        st = lib.linear_forward_grouped(ptrs(xs), ptrs(ws), ptrs(outs), (ctypes.c_int * g)(*[x.shape[0] for x in xs]),
+                                        g, n, k, lds(xs), lds(ws), lds(outs), _dtype_code(xs[0]),
+                                        _stream_handle(dev, stream))
+    check(st)
+    return outs
 
 
 def mha_forward_workspace_size(batch: int, n_q: int, n_k: int, d_model: int, heads: int, dtype) -> int:

@@ -45,6 +45,8 @@ SIGNATURES = {
                                         _vp, _vp, _vp]),
     "linear_forward": (_int, [_vp, _vp, _vp, _int, _int, _int, ctypes.c_int64, ctypes.c_int64,
                               ctypes.c_int64, _int, _vp]),
+    "linear_forward_grouped": (_int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                      ctypes.POINTER(_int), _int, _int, _int, _i64x3, _i64x3, _i64x3, _int, _vp]),
     "mha_forward_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int, _int, _int]),
     "mha_forward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                            _int, _int, _int, _int, _int, _int, _int, _vp]),

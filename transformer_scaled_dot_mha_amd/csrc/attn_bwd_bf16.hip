@@ -180,15 +180,14 @@ __device__ __forceinline__ int swz(int r) {
 }
 __device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(size_t)(const lds_char*)p; }
 // 16 (or 4) bytes per lane from a raw buffer into LDS at lds_byte + 16 (or 4)
-// times the lane (m0 holds the wave-uniform base); offsets past the buffer's
-// record write zeros.
+// times the lane; offsets past the buffer's record write zeros. The
+// wave-uniform LDS base goes in m0 through the asm's {m0} operand, so the
+// compiler sets m0 itself and knows the register is taken.
 __device__ __forceinline__ void dma16(u32x4 rsrc, unsigned voff, unsigned lds_byte) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_byte)
-               : "memory");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_byte) : "memory");
 }
 __device__ __forceinline__ void dma4(u32x4 rsrc, unsigned voff, unsigned lds_byte) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_byte)
-               : "memory");
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_byte) : "memory");
 }
 // Raw buffer descriptor (stride 0) over `bytes` bytes from base.
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {

@@ -75,11 +75,12 @@ __device__ __forceinline__ u32x4 gather_row_chunk(unsigned a0, unsigned a1, unsi
 __device__ __forceinline__ unsigned lds_off(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
 }
-// 16 bytes per lane from a raw buffer into LDS at lds_byte + 16 * lane (m0
-// holds the wave-uniform LDS base); offsets past the record write zeros.
+// 16 bytes per lane from a raw buffer into LDS at lds_byte + 16 * lane;
+// offsets past the record write zeros. The wave-uniform LDS base goes in m0
+// through the asm's {m0} operand, so the compiler sets m0 itself and knows
+// the register is taken.
 __device__ __forceinline__ void dma16(u32x4 rsrc, unsigned voff, unsigned lds_byte) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_byte)
-               : "memory");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_byte) : "memory");
 }
 // Raw buffer descriptor (stride 0) over `bytes` bytes from base.
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {

@@ -547,6 +547,32 @@ mha_status linear_forward(const void* x, const void* w, void* y, int m, int n, i
   }
 }
 
+mha_status linear_forward_grouped(const void* const* x, const void* const* w, void* const* y, const int* m,
+                                  int groups, int n, int k, const int64_t* ldx, const int64_t* ldw,
+                                  const int64_t* ldy, mha_dtype dtype, void* stream) {
+  try {
+    if (!x || !w || !y || !m || !ldx || !ldw || !ldy)
+      return fail(MHA_ERR_INVALID_ARG, "x, w, y, m, ldx, ldw and ldy must be non-null arrays");
+    if (groups < 1 || groups > 3) return fail(MHA_ERR_INVALID_ARG, "groups must be 1, 2 or 3 (got %d)", groups);
+    mha::LinearArgs a = {};
+    int max_m = 0;
+    for (int g = 0; g < groups; ++g) {
+      mha_status s = validate_linear(x[g], w[g], y[g], m[g], n, k, ldx[g], ldw[g], ldy[g], (int)dtype);
+      if (s != MHA_OK) return s;
+      a.g[g] = mha::LinearGroup{x[g], w[g], y[g], m[g], ldx[g], ldw[g], ldy[g]};
+      max_m = m[g] > max_m ? m[g] : max_m;
+    }
+    const int64_t tiles = (int64_t)groups * ((max_m + 63) / 64) * ((n + 63) / 64);
+    if (tiles > INT32_MAX) return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+    a.groups = groups;
+    a.n = n;
+    a.k = k;
+    return run_linear(a, dtype, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in linear_forward_grouped");
+  }
+}
+
 size_t mha_forward_workspace_size(int batch, int n_q, int n_k, int d_model, int heads, mha_dtype dtype) {
   if (batch < 1 || n_q < 1 || n_k < 1 || d_model < 1 || heads < 1 || !valid_dtype((int)dtype)) return 0;
   WsLayout w;
