@@ -305,7 +305,6 @@ def cpu_baseline(w, inputs, min_seconds=10.0, max_seconds=30.0):
 
 def env_info():
     """ROCm and HIP versions and the device, for the record."""
-    import subprocess
     import torch
     info = {"torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None)}
     try:
@@ -313,13 +312,16 @@ def env_info():
             info["rocm"] = f.read().strip()
     except OSError:
         info["rocm"] = None
+    # the compiler that built libmha.so, as the build recorded it (no compiler is
+    # run from this process: it has initialised the GPU)
     try:
-        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=60).stdout
+        with open(os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "libmha.build.json")) as f:
+            out = "\n".join(json.load(f).get("hipcc_version", []))
         m = re.search(r"HIP version:\s*(\S+)", out)
         info["hipcc_hip_version"] = m.group(1) if m else None
         m = re.search(r"clang version\s*(\S+)", out)
         info["hipcc_clang"] = m.group(1) if m else None
-    except (OSError, subprocess.SubprocessError):
+    except (OSError, ValueError):
         info["hipcc_hip_version"] = None
     p = torch.cuda.get_device_properties(0)
     info["gpu"] = p.name

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import glob
+import json
 import os
 import shutil
 import subprocess
@@ -18,6 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmha.so")
+BUILD_INFO = os.path.join(HERE, "libmha.build.json")
 OBJDIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -68,6 +70,17 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    # the toolchain that built the library, for the bench record (read there
+    # without running the compiler from a process that uses the GPU)
+    ver = subprocess.run([_hipcc(), "--version"], capture_output=True, text=True).stdout
+    info = {"hipcc_version": ver.strip().splitlines(), "arch": ARCH, "flags": COMMON + DEVICE_FLAGS}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f, indent=1)
     return LIB
 
 
