@@ -200,6 +200,26 @@ mha_status mha_forward_padded(const void* xq, const void* xk, const void* xv, co
                               const int32_t* kv_len, void* stream);
 
 /*
+ * mha_forward_noalloc -- mha_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation, arguments and rules, minus the
+ * workspace. The library keeps the intermediates (Q, K, V, the concatenated
+ * heads) in a fixed device array of MHA_NOALLOC_MAX_WORKSPACE bytes, one per
+ * GPU, held from the library's load on that GPU until the process ends. The
+ * call allocates nothing.
+ * A problem whose mha_forward_workspace_size exceeds the array is rejected
+ *   with MHA_ERR_UNSUPPORTED before any HIP call (use mha_forward there).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ *   (different streams or threads without ordering between them) race and
+ *   give undefined results. Calls ordered on one stream are safe.
+ */
+#define MHA_NOALLOC_MAX_WORKSPACE ((size_t)128 << 20)
+mha_status mha_forward_noalloc(const void* xq, const void* xk, const void* xv, const void* wq,
+                               const void* wk, const void* wv, const void* wo, void* out, int batch,
+                               int n_q, int n_k, int d_model, int heads, mha_dtype dtype, int causal,
+                               void* stream);
+
+/*
  * encoder_layer_forward -- one Transformer encoder layer, post-norm, inference:
  *   h   = LayerNorm(x + MultiHead(x, x, x))            (attention with biases)
  *   out = LayerNorm(h + FFN(h)),  FFN(h) = max(0, h W1 + b1) W2 + b2

@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_boundary():
     fns = header_functions()
     assert {"attention_forward", "attention_forward_padded", "mha_forward", "mha_forward_padded",
-            "mha_forward_workspace_size", "linear_forward", "linear_forward_grouped", "encoder_layer_workspace_size",
+            "mha_forward_workspace_size", "mha_forward_noalloc", "linear_forward", "linear_forward_grouped", "encoder_layer_workspace_size",
             "encoder_layer_forward", "attention_decode_workspace_size", "attention_decode",
             "attention_backward_workspace_size", "attention_backward",
             "mha_status_string", "mha_last_error", "mha_version"} == set(fns)
@@ -354,3 +354,21 @@ def test_backward_validation(lib, kw, status, needle):
 def test_backward_workspace_size(lib):
     assert lib.attention_backward_workspace_size(2, 8, 100) == (2 * 8 * 100 * 8 + 255) // 256 * 256
     assert lib.attention_backward_workspace_size(0, 8, 100) == 0
+
+
+def test_noalloc_rejects_oversized_problems_before_any_device_call(lib):
+    """mha_forward_noalloc serves workspaces up to MHA_NOALLOC_MAX_WORKSPACE bytes
+    (its fixed per-GPU array); a larger problem is refused on the host."""
+    header = open(HEADER).read()
+    assert "#define MHA_NOALLOC_MAX_WORKSPACE ((size_t)128 << 20)" in header
+    assert _lib.NOALLOC_MAX_WORKSPACE == 128 << 20
+    args = lambda B, n, dm, h, dt=1: (FAKE,) * 8 + (B, n, n, dm, h, dt, 0, None)
+    # the encoder workload (B=32, N=512, d_model 512, bf16) needs exactly 64 MiB: served
+    assert lib.mha_forward_workspace_size(32, 512, 512, 512, 8, 1) == 64 << 20
+    # 2.5x that is refused
+    assert lib.mha_forward_noalloc(*args(80, 512, 512, 8)) == _lib.MHA_ERR_UNSUPPORTED
+    assert "128 MiB" in lib.mha_last_error().decode()
+    assert lib.mha_forward_noalloc(*args(0, 512, 512, 8)) == _lib.MHA_ERR_INVALID_ARG
+    assert lib.mha_forward_noalloc(*args(1, 16, 512, 8, dt=9)) == _lib.MHA_ERR_INVALID_ARG
+    null_out = (FAKE,) * 7 + (None, 1, 16, 16, 512, 8, 1, 0, None)
+    assert lib.mha_forward_noalloc(*null_out) == _lib.MHA_ERR_INVALID_ARG

@@ -12,13 +12,13 @@ import ctypes
 import math
 
 from ._lib import (ENCODER_WEIGHT_NAMES, EncoderWeights, KVCache, MHA_BF16, MHA_ERR_HIP, MHA_ERR_INVALID_ARG,
-                   MHA_ERR_UNSUPPORTED,
+                   MHA_ERR_UNSUPPORTED, NOALLOC_MAX_WORKSPACE,
                    MHA_ERR_WORKSPACE, MHA_F32, MHA_OK, LIB_PATH, MHAError, check, load, strides3)
 
 __all__ = ["attention_backward", "attention_backward_workspace_size", "attention_decode",
            "attention_decode_workspace_size", "attention_forward", "encoder_layer_forward", "encoder_layer_workspace_size",
            "linear_forward", "linear_forward_grouped",
-           "mha_forward", "mha_forward_workspace_size",
+           "mha_forward", "mha_forward_noalloc", "mha_forward_workspace_size",
            "MHAError", "MHA_F32", "MHA_BF16", "LIB_PATH", "load"]
 
 
@@ -286,6 +286,36 @@ def mha_forward(xq, xk, xv, wq, wk, wv, wo, heads: int, *, causal: bool = False,
             st = lib.mha_forward(*args, _stream_handle(dev, stream))
         else:
             st = lib.mha_forward_padded(*args, _kv_len_arg(kv_len, B, dev), _stream_handle(dev, stream))
+    check(st)
+    return out
+
+
+def mha_forward_noalloc(xq, xk, xv, wq, wk, wv, wo, heads: int, *, causal: bool = False, out=None, stream=None):
+    """mha_forward without a workspace: the library keeps the intermediates in its
+    own fixed per-GPU device array (NOALLOC_MAX_WORKSPACE bytes), so the call
+    allocates nothing on the device when `out` is given. Calls that overlap on
+    one GPU race on that array."""
+    torch = _torch()
+    dev = _require_device(xq, xk, xv, wq, wk, wv, wo)
+    B, n_q, d_model = xq.shape
+    n_k = xk.shape[1]
+    if xk.shape != (B, n_k, d_model) or xv.shape != xk.shape:
+        raise ValueError("xk and xv must be (B, N_k, d_model)")
+    for w in (wq, wk, wv, wo):
+        if tuple(w.shape) != (d_model, d_model):
+            raise ValueError("weights must be (d_model, d_model)")
+    for t in (xq, xk, xv, wq, wk, wv, wo):
+        if not t.is_contiguous():
+            raise ValueError("mha_forward_noalloc takes contiguous tensors")
+    if out is None:
+        out = torch.empty((B, n_q, d_model), dtype=xq.dtype, device=dev)
+    if tuple(out.shape) != (B, n_q, d_model) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B, N_q, d_model) tensor")
+    lib = load()
+    with _on_device(dev):
+        st = lib.mha_forward_noalloc(xq.data_ptr(), xk.data_ptr(), xv.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+                                     wv.data_ptr(), wo.data_ptr(), out.data_ptr(), B, n_q, n_k, d_model, heads,
+                                     _dtype_code(xq), int(bool(causal)), _stream_handle(dev, stream))
     check(st)
     return out
 

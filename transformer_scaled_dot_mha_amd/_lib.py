@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
 
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_WORKSPACE, MHA_ERR_HIP = range(5)
 MHA_F32, MHA_BF16 = 0, 1
+NOALLOC_MAX_WORKSPACE = 128 << 20  # MHA_NOALLOC_MAX_WORKSPACE of include/mha.h
 
 _i64x3 = ctypes.POINTER(ctypes.c_int64)
 _vp = ctypes.c_void_p
@@ -50,6 +51,8 @@ SIGNATURES = {
     "mha_forward_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int, _int, _int]),
     "mha_forward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                            _int, _int, _int, _int, _int, _int, _int, _vp]),
+    "mha_forward_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int,
+                                   _int, _vp]),
     "mha_forward_padded": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   _int, _int, _int, _int, _int, _int, _int, _vp, _vp]),
     "encoder_layer_workspace_size": (ctypes.c_size_t, [_int, _int, _int, _int, _int, _int]),

@@ -486,6 +486,21 @@ mha_status backward_impl(const void* q, const void* k, const void* v, const void
 
 }  // namespace
 
+namespace mha {
+// Entry points defined in other sources of the library use these two: the
+// thread-local error text, and mha_forward's body (with its validation) on a
+// workspace they supply.
+mha_status report_error(mha_status s, const char* msg) { return fail(s, "%s", msg); }
+
+mha_status mha_forward_on_workspace(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk,
+                                    const void* wv, const void* wo, void* out, void* workspace,
+                                    size_t workspace_bytes, int batch, int n_q, int n_k, int d_model, int heads,
+                                    mha_dtype dtype, int causal, void* stream) {
+  return mha_impl(xq, xk, xv, wq, wk, wv, wo, out, workspace, workspace_bytes, batch, n_q, n_k, d_model, heads, dtype,
+                  causal, nullptr, stream);
+}
+}  // namespace mha
+
 extern "C" {
 
 const char* mha_status_string(mha_status s) {
