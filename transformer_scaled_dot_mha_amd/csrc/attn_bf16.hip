@@ -7,36 +7,43 @@
 // row maximum and row sum (the tiling idea the pages credit to FlashAttention,
 // "32 Transformer", "Connections"; re-derived here for CDNA4).
 //
-// Work decomposition
-//   workgroup = 256 threads = 4 wavefronts of one (batch, head); each
-//   wavefront owns 32 query rows, or 64 (two 32-row blocks sharing every K/V
-//   fragment read) for long query runs, so a workgroup owns 128 or 256 rows.
-//   key/value tiles of 64 rows are staged through LDS, double buffered, with
-//   the next tile's global loads (raw buffer loads; rows past the end read as
-//   zero) in flight while the current one is used.
+// Two kernel forms, both with workgroups of 4 wavefronts on one (batch, head)
+// and 64-key tiles staged through LDS:
+//   32 query rows per wavefront (128 per workgroup): short or ragged query
+//     runs. Tiles are double buffered: the next tile's global loads (raw
+//     buffer loads; rows past the end read as zero) are in flight in
+//     registers while the current one is used, then written to LDS, V
+//     transposed ([d][key], two keys per 32-bit word).
+//   64 query rows per wavefront (two 32-row blocks sharing every K/V fragment
+//     read; 256 per workgroup): long query runs. Tiles go straight from global
+//     memory into a 4-stage LDS ring (buffer loads that write LDS) three tiles
+//     ahead; the wavefront walks 32-key slabs and reads the next slab's K and
+//     V fragments while the current one is computed.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, fp32 accumulate)
 //   Scores are formed transposed, S^T = K Q^T: the MFMA's B operand is the
 //   wavefront's Q^T (kept in registers for the whole kernel) and its A operand
 //   is a 32-key slab of K read from LDS. In the 32x32 accumulator layout lane l
 //   then holds column n = l % 32 (one query) and 16 rows (keys), so a query's
-//   row maximum and row sum are in-register reductions plus one exchange
-//   between lane halves.
-//   K rows are written to LDS in a permuted order so that accumulator register
+//   row maximum is an in-register reduction plus one exchange between lane
+//   halves.
+//   K rows are placed in LDS in a permuted order so that accumulator register
 //   r of lane half hf holds key 16*(r/8) + 8*hf + (r%8) of its 32-key slab.
 //   After conversion to bf16 those registers are, unchanged, the B operand of
 //   O^T = V^T P^T (8 consecutive keys per lane), so P never goes through LDS.
-//   V is transposed into LDS ([d][key]) while staging, two keys per 32-bit word.
 //
-// Softmax: exp2 with scale*log2(e) folded into one FMA; the row sum is
-// accumulated from the bf16-rounded weights that the P V product uses, so the
-// final 1/l normalises exactly what was summed. The reference maximum is
-// moved lazily (only when weights against it would grow past 2^8), so the
-// rescale of O and l is skipped on almost every tile; numerator and
-// denominator always share one reference, so the result stays exact.
+// Softmax: exp2 with scale*log2(e) folded into one FMA. The row sum is formed
+// on the matrix core from the bf16-rounded weights that the P V product uses
+// (so the final 1/l normalises exactly what was multiplied by V). The
+// reference maximum is moved lazily (only when weights against it would grow
+// past 2^8), so the rescale of O and l is skipped on almost every slab;
+// numerator and denominator always share one reference, so the result stays
+// exact.
 // Causal: tiles wholly above the diagonal are never loaded; per wavefront, a
 // tile whose first key lies past the wavefront's last query is skipped; only
 // tiles that straddle the diagonal (or the ragged end) apply per-element masks.
+// Causal workgroups run heaviest query block first, with each head's blocks
+// on one XCD.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -50,6 +57,7 @@ typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
@@ -69,10 +77,25 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
 }
 
-// Sum of a packed bf16 pair, added to acc in fp32 (v_dot2c_f32_bf16 with (1, 1)).
-__device__ __forceinline__ float add_pair(unsigned pair, float acc) {
-  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+// Row sums of one 32-key slab's bf16 weights on the matrix core (v_dot2c
+// would stall behind every MFMA in flight). The weights' registers, the B
+// operand of the P V products (8 keys of one query per lane), are fed
+// unchanged as the B operand of two v_mfma_f32_16x16x32_bf16 (one per 16
+// keys) against a constant 0/1 selector A: lane l of that B holds column
+// j = l % 16, rows 8 (l / 16) + 0..7, i.e. query 16 ((l / 16) % 2) + j, keys
+// 8 (l / 32) + 0..7. Selector row m (m % 4 == 0) takes the groups whose
+// query half is (m / 4) % 2, so output register 0 of lane L holds the slab's
+// sum for query L % 32 in both lane halves. Products with 1 are exact and the
+// accumulation is fp32, as with the dot instruction.
+__device__ __forceinline__ bf16x8 rowsum_selector(int lane) {
+  const unsigned one = ((lane & 3) == 0 && ((lane >> 2) & 1) == ((lane >> 4) & 1)) ? 0x3F803F80u : 0u;
+  return __builtin_bit_cast(bf16x8, u32x4{one, one, one, one});
+}
+__device__ __forceinline__ float slab_rowsum(const unsigned (&pw)[8], const bf16x8& sel) {
+  const bf16x8 p0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+  const bf16x8 p1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+  const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p0, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p1, c, 0, 0, 0)[0];
 }
 
 // LDS row that receives key offset kappa (0..31) of a 32-key slab, so that the
@@ -88,11 +111,6 @@ __device__ __forceinline__ float max_halves(float x) {
                                                   false, false);
   return __builtin_fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
-__device__ __forceinline__ float sum_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
-                                                  false, false);
-  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
 
 // The reference maximum moves only when a row's weights against it would
 // exceed 2^8, so the rescale of O and l is skipped on almost every tile. The
@@ -104,15 +122,14 @@ struct RowState {
   f32x16 o0, o1;
   float m;   // reference maximum (raw score units), identical in both lane halves
   float mc;  // m * c
-  float l;   // running sum over this lane half's keys
+  float l;   // running row sum (the same in both lane halves)
 };
 
 // Softmax weights of pairs [i0, i1) of one 32-key slab (16 scores per lane)
-// against the current reference, rounded to bf16; ps adds exactly the
-// rounded values.
+// against the current reference, rounded to bf16.
 template <bool kMasked>
-__device__ __forceinline__ void slab_weights(const float (&sv)[16], unsigned (&pw)[8], float& ps, float mc, float c,
-                                             int i0, int i1) {
+__device__ __forceinline__ void slab_weights(const float (&sv)[16], unsigned (&pw)[8], float mc, float c, int i0,
+                                             int i1) {
 #pragma unroll
   for (int i = i0; i < i1; ++i) {
     float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c, -mc));
@@ -122,35 +139,32 @@ __device__ __forceinline__ void slab_weights(const float (&sv)[16], unsigned (&p
       p1 = sv[2 * i + 1] == -INFINITY ? 0.f : p1;
     }
     pw[i] = pack_bf16(p0, p1);
-    ps = add_pair(pw[i], ps);
   }
 }
 
-struct NoPending {
-  __device__ void operator()() const {}
-};
-
 // Every weight is <= 2^8 while the reference holds. A weight above 2^8 (or
-// an overflow) makes the lane's 16-weight sum exceed 2^8, so one compare per
+// an overflow) makes the row's 32-weight slab sum exceed 2^8, so one compare per
 // slab detects when the reference must move; only then is the row maximum
 // formed, O and l rescaled and the slab's weights recomputed. This branch is
-// taken on the first tile and rarely after.
-// `flush_pending` adds into O the weights of an earlier slab that were
-// computed against the current reference but not yet multiplied by V; it
-// runs before a move, so that O is rescaled together with them (l already
-// holds their sum).
-template <bool kMasked, typename Pending = NoPending>
-__device__ __forceinline__ void check_reference(RowState& st, const float (&sv)[16], unsigned (&pw)[8], float& ps,
-                                                float c, Pending&& flush_pending = Pending{}) {
+// taken on a block's first slab and rarely after. Both kernel forms check a
+// block's slab before forming that block's next weights and add its weights
+// into O right after the check, so nothing computed against an older
+// reference is left outside O and l when they are rescaled. The slab's scores
+// are not kept for this path: `rescore` forms them again from the staged tile.
+template <bool kMasked, typename Rescore>
+__device__ __forceinline__ void check_reference(RowState& st, Rescore&& rescore, unsigned (&pw)[8], float ps, float c,
+                                                const bf16x8& sel) {
   const bool bad = !(ps <= kMaxSlabSum) || st.m == -INFINITY;
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
     asm volatile("" ::: "memory");  // keep a real branch, not predicated code
+    // the slab's scores again (their registers are not kept for this rare path)
+    float sv[16];
+    rescore(sv);
     float tmax = sv[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) tmax = __builtin_fmaxf(tmax, sv[r]);
     tmax = max_halves(tmax);
     const float m_new = __builtin_fmaxf(st.m, tmax);
-    if (__builtin_amdgcn_ballot_w64(m_new > st.m) != 0) flush_pending();
     if (m_new > st.m) {
       const float mc_new = m_new * c;
       const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.mc - mc_new);
@@ -160,8 +174,8 @@ __device__ __forceinline__ void check_reference(RowState& st, const float (&sv)[
       st.m = m_new;
       st.mc = mc_new;
     }
-    ps = 0.f;
-    slab_weights<kMasked>(sv, pw, ps, st.mc, c, 0, 8);
+    slab_weights<kMasked>(sv, pw, st.mc, c, 0, 8);
+    ps = slab_rowsum(pw, sel);
   }
   st.l += ps;
 }
@@ -210,29 +224,18 @@ __device__ __forceinline__ void scores_of_impl(float (&sv)[16], const f32x16& s,
   }
 }
 
-// One 64-key tile for one wavefront holding kQB blocks of 32 query rows.
-// Each block's tile is two 32-key slabs (register r of a slab holds key
-// 32*slab + 16*(r/8) + 8*hf + r%8 of the tile). K and V fragments are read
-// from LDS once and used by every block of the wavefront.
-//
-// Unmasked tiles are issued in a fixed order so that the wavefront keeps both
-// the matrix core and the VALU busy: every MFMA is followed by a chunk of
-// softmax work that does not depend on it.
-//   kQB = 1: slab 0's S^T MFMAs; slab 1's S^T MFMAs each followed by a
-//            quarter of slab 0's softmax; slab 0's P V MFMAs each followed by
-//            a quarter of slab 1's softmax; slab 1's P V MFMAs.
-//   kQB = 2: block A's S^T MFMAs; block B's eight S^T MFMAs each followed by
-//            an eighth of A's softmax; A's eight P V MFMAs each followed by an
-//            eighth of B's softmax; B's P V MFMAs.
-// A reference move (rare) rescales that block's O and l after its earlier
-// P V products, so every term matches the reference it was computed against:
-// with kQB = 2 both slabs of a block are checked before its P V products, so
-// a move found on slab 1 first adds slab 0's weights into O.
-// kMasked (diagonal and ragged-end tiles) runs the same order, with masked
-// keys' scores set to -inf before the softmax.
+// One 64-key tile for a wavefront of the 32-row form: two 32-key slabs
+// (register r of a slab holds key 32*slab + 16*(r/8) + 8*hf + r%8 of the
+// tile). Issue order, so that the wavefront keeps both the matrix core and the
+// VALU busy: slab 0's S^T MFMAs; slab 1's S^T MFMAs each followed by a quarter
+// of slab 0's softmax; slab 0's row sum and check; slab 0's P V MFMAs each
+// followed by a quarter of slab 1's softmax; slab 1's row sum and check; slab
+// 1's P V MFMAs. kMasked (diagonal and ragged-end tiles) runs the same order,
+// with masked keys' scores set to -inf before the softmax.
 template <bool kMasked, int kQB, bool kFirst = false>
 __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&qf)[kQB][4], const bf16* Ks,
-                                            const bf16* Vt, const int (&last)[kQB], int lq, int hf, float c) {
+                                            const bf16* Vt, const int (&last)[kQB], int lq, int hf, float c,
+                                            const bf16x8& sel) {
   // the slab's scores; on a wavefront's first (unmasked) tile, slab 0 also
   // sets its block's reference, so that its weights need no second pass
   auto scores_of = [&](float (&sv)[16], const f32x16& s, int slab, int lst, RowState& rs) {
@@ -244,8 +247,16 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
   for (int slab = 0; slab < 2; ++slab)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) kf[slab][kk] = ld16(Ks + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf);
+  auto rescore = [&](int qb, int slab) {
+    return [&, qb, slab](float (&sv)[16]) {
+      f32x16 s = {};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) s = qk_one(s, ld16(Ks + (32 * slab + lq) * kPitch + 16 * kk + 8 * hf), qf[qb][kk]);
+      scores_of_impl<kMasked>(sv, s, slab, last[qb]);
+    };
+  };
 
-  if (kQB == 1) {
+  {
     u32x4 vf0[2][2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
@@ -256,16 +267,15 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
     for (int kk = 0; kk < 4; ++kk) s0 = qk_one(s0, kf[0][kk], qf[0][kk]);
     float sv0[16], sv1[16];
     unsigned pw0[8], pw1[8];
-    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       s1 = qk_one(s1, kf[1][kk], qf[0][kk]);
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 0) scores_of(sv0, s0, 0, last[0], st[0]);
-      slab_weights<kMasked>(sv0, pw0, ps0, st[0].mc, c, 2 * kk, 2 * kk + 2);
+      slab_weights<kMasked>(sv0, pw0, st[0].mc, c, 2 * kk, 2 * kk + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    check_reference<kMasked>(st[0], sv0, pw0, ps0, c);
+    check_reference<kMasked>(st[0], rescore(0, 0), pw0, slab_rowsum(pw0, sel), c, sel);
     u32x4 vf1[2][2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
@@ -276,80 +286,12 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
     for (int i = 0; i < 4; ++i) {
       pv_one(st[0], vf0[i >> 1][i & 1], pw0, i >> 1, i & 1);
       __builtin_amdgcn_sched_barrier(0);
-      slab_weights<kMasked>(sv1, pw1, ps1, st[0].mc, c, 2 * i, 2 * i + 2);
+      slab_weights<kMasked>(sv1, pw1, st[0].mc, c, 2 * i, 2 * i + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    check_reference<kMasked>(st[0], sv1, pw1, ps1, c);
+    check_reference<kMasked>(st[0], rescore(0, 1), pw1, slab_rowsum(pw1, sel), c, sel);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv_one(st[0], vf1[i >> 1][i & 1], pw1, i >> 1, i & 1);
-  } else {
-    // block A = 0, block B = kQB - 1
-    constexpr int A = 0, B = kQB - 1;
-    f32x16 sa[2] = {}, sb[2] = {};
-#pragma unroll
-    for (int slab = 0; slab < 2; ++slab)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sa[slab] = qk_one(sa[slab], kf[slab][kk], qf[A][kk]);
-    u32x4 vf[2][2][2];  // [slab][jj][blk]
-#pragma unroll
-    for (int slab = 0; slab < 2; ++slab)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-          vf[slab][jj][blk] = ld16(Vt + (32 * blk + lq) * kPitch + 16 * (2 * slab + jj) + 8 * hf);
-    float sva[2][16], svb[2][16];
-    unsigned pwa[2][8], pwb[2][8];
-    float psa[2] = {0.f, 0.f}, psb[2] = {0.f, 0.f};
-    // slab 0's weights of a block, added into O (and cleared) ahead of a
-    // reference move found on its slab 1
-    auto pending_a = [&] {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pv_one(st[A], vf[0][j >> 1][j & 1], pwa[0], j >> 1, j & 1);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pwa[0][j] = 0u;
-    };
-    auto pending_b = [&] {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pv_one(st[B], vf[0][j >> 1][j & 1], pwb[0], j >> 1, j & 1);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pwb[0][j] = 0u;
-    };
-    // B's S^T, each MFMA followed by a quarter slab of A's softmax
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int slab = i >> 2, kk = i & 3;
-      sb[slab] = qk_one(sb[slab], kf[slab][kk], qf[B][kk]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) scores_of(sva[slab], sa[slab], slab, last[A], st[A]);
-      slab_weights<kMasked>(sva[slab], pwa[slab], psa[slab], st[A].mc, c, 2 * kk, 2 * kk + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk == 3) {
-        if (slab == 0)
-          check_reference<kMasked>(st[A], sva[0], pwa[0], psa[0], c);
-        else
-          check_reference<kMasked>(st[A], sva[1], pwa[1], psa[1], c, pending_a);
-      }
-    }
-    // A's P V, each MFMA followed by a quarter slab of B's softmax
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int slab = i >> 2, jj = (i >> 1) & 1, blk = i & 1, q4 = i & 3;
-      pv_one(st[A], vf[slab][jj][blk], pwa[slab], jj, blk);
-      __builtin_amdgcn_sched_barrier(0);
-      if (q4 == 0) scores_of(svb[slab], sb[slab], slab, last[B], st[B]);
-      slab_weights<kMasked>(svb[slab], pwb[slab], psb[slab], st[B].mc, c, 2 * q4, 2 * q4 + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      if (q4 == 3) {
-        if (slab == 0)
-          check_reference<kMasked>(st[B], svb[0], pwb[0], psb[0], c);
-        else
-          check_reference<kMasked>(st[B], svb[1], pwb[1], psb[1], c, pending_b);
-      }
-    }
-    // B's P V
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pv_one(st[B], vf[i >> 2][(i >> 1) & 1][i & 1], pwb[i >> 2], (i >> 1) & 1, i & 1);
   }
 }
 
@@ -361,9 +303,10 @@ __device__ __forceinline__ u32x4 gather_row_chunk(unsigned a0, unsigned a1, unsi
   return u32x4{(unsigned)x0[0], (unsigned)x1[0], (unsigned)x0[1], (unsigned)x1[1]};
 }
 
-// kQB blocks of 32 query rows per wavefront, 4 wavefronts per workgroup.
-template <bool kCausal, int kQB>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c, unsigned q_sign, int n_qblk) {
+// The 32-row form: 32 query rows per wavefront, 4 wavefronts per workgroup.
+template <bool kCausal>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r32(AttnArgs a, float c, unsigned q_sign, int n_qblk) {
+  constexpr int kQB = 1;
   constexpr int kRowsPerWave = 32 * kQB;
   constexpr int kRows = 4 * kRowsPerWave;  // query rows per workgroup
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * kTile];
@@ -374,14 +317,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
   const int lq = lane & 31;
   const int hf = lane >> 5;
   const int n_q = a.n_q;
+  const bf16x8 sel = rowsum_selector(lane);
 
   // ---- workgroup -> (batch*head, query block)
   int bh, qblk;
   if (kCausal) {
-    // heaviest query blocks (most key tiles) are dispatched first
+    // heaviest query blocks (most key tiles) are dispatched first; workgroup i
+    // goes to XCD i % 8, so XCD x takes the heads bh = x (mod 8) and all of a
+    // head's query blocks share one L2
     const int BH = a.batch * a.heads;
-    qblk = n_qblk - 1 - (int)(blockIdx.x / BH);
-    bh = (int)(blockIdx.x % BH);
+    if ((BH & 7) == 0) {
+      const int x = blockIdx.x & 7, j = blockIdx.x >> 3, bhx = BH >> 3;
+      qblk = n_qblk - 1 - j / bhx;
+      bh = x + 8 * (j % bhx);
+    } else {
+      qblk = n_qblk - 1 - (int)(blockIdx.x / BH);
+      bh = (int)(blockIdx.x % BH);
+    }
   } else {
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
     // contiguous run of logical ids so the query blocks of one (batch, head)
@@ -484,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
   if (t_split > 0) {  // the first tile sets each block's reference from its first slab
     const bool more = 1 < ntiles;
     if (more) gload(kBN);
-    attend_tile<false, kQB, true>(st, qf, smem, smem + kTile, no_mask, lq, hf, c);
+    attend_tile<false, kQB, true>(st, qf, smem, smem + kTile, no_mask, lq, hf, c, sel);
     if (more) lstore(1);
     __syncthreads();
     t = 1;
@@ -493,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
     const bool more = t + 1 < ntiles;
     if (more) gload((t + 1) * kBN);
     const bf16* Ks = smem + (t & 1) * 2 * kTile;
-    attend_tile<false, kQB>(st, qf, Ks, Ks + kTile, no_mask, lq, hf, c);
+    attend_tile<false, kQB>(st, qf, Ks, Ks + kTile, no_mask, lq, hf, c, sel);
     if (more) lstore((t + 1) & 1);
     __syncthreads();
   }
@@ -507,7 +459,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb)
         last[qb] = (kCausal ? min(n_k - 1, q_wave0 + 32 * qb + lq) : n_k - 1) - k0 - 8 * hf;
-      attend_tile<true, kQB>(st, qf, Ks, Ks + kTile, last, lq, hf, c);
+      attend_tile<true, kQB>(st, qf, Ks, Ks + kTile, last, lq, hf, c, sel);
     }
     if (more) lstore((t + 1) & 1);
     __syncthreads();
@@ -518,7 +470,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int my_q = q_wave0 + 32 * qb + lq;
-    const float l_tot = sum_halves(st[qb].l);
+    const float l_tot = st[qb].l;
     // a row with no visible key (padded length 0) has l = 0: output 0, lse -inf
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     unsigned w[2][4][2];
@@ -549,29 +501,335 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64(AttnArgs a, float c,
   }
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// LDS stage: K tile (64 rows x 128 B, rows in the permuted key order), then V
+// tile (64 rows x 128 B, key order); 16-byte chunk c of row R sits at chunk
+// position c ^ (R & 7).
+constexpr int kRowBytes = 128;
+constexpr int kStageBytes = 2 * 64 * kRowBytes;
+constexpr int kNStages = 4;
+struct LdsFrags {
+  const char* base;  // generic pointer to the stage
+  int klane[4];      // per-lane byte offsets of K fragments kk = 0..3 (slab 0)
+  int vlane;         // per-lane byte offset of V transposed reads
+  __device__ __forceinline__ u32x4 k(int slab, int kk) const {
+    return *reinterpret_cast<const u32x4*>(base + klane[kk] + slab * 32 * kRowBytes);
+  }
+  __device__ __forceinline__ u32x4 v(int slab, int jj, int blk) const {
+    const char* p = base + 64 * kRowBytes + vlane + (32 * slab + 16 * jj) * kRowBytes;
+    const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 64 * blk));
+    const v4i16 x1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 4 * kRowBytes + 64 * (blk ^ 1)));
+    const u32x2 a = __builtin_bit_cast(u32x2, x0), b = __builtin_bit_cast(u32x2, x1);
+    return u32x4{a[0], a[1], b[0], b[1]};
+  }
+};
+
+__device__ __forceinline__ unsigned lds_off(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+// 16 bytes per lane from a raw buffer into LDS at lds_byte + 16 * lane (rows
+// past the record end write zeros). Issued as asm so that the compiler does
+// not wait for it before every LDS read; completion is awaited explicitly
+// (vmcnt). The wave-uniform LDS base goes in m0 through the {m0} operand, so
+// the compiler sets m0 itself and knows the register is taken.
+__device__ __forceinline__ void dma16(u32x4 rsrc, int voff, unsigned lds_byte) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_byte) : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// 64 query rows per wavefront (blocks A and B of 32), slab-pipelined: the
+// wavefront walks 32-key slabs; K and V fragments of slab g + 1 are read while
+// slab g is computed, so no fragment read waits at a slab's start. Per slab:
+//   A's 4 S^T MFMAs;
+//   B's 4 S^T MFMAs, each followed by a quarter of A's softmax; A's row sum;
+//   a quarter of B's softmax, A's check; A's 4 P V MFMAs each followed by
+//     the next quarter of B's softmax (the last after them); B's row sum;
+//   B's check; B's 4 P V MFMAs.
+// Tiles of 64 keys (two slabs) are staged by DMA into a 4-stage LDS ring
+// three tiles ahead; at tile t's sync tiles t and t + 1 are complete, so
+// slab 1 of tile t can read tile t + 1's fragments.
+template <bool kMasked, bool kFirst>
+__device__ __forceinline__ void attend_slab(RowState (&st)[2], const u32x4 (&qf)[2][4], const LdsFrags& fr, int slab,
+                                            const int (&last)[2], float c, const bf16x8& sel, const u32x4 (&kf)[4],
+                                            const u32x4 (&vf)[2][2], u32x4 (&kf_nxt)[4], u32x4 (&vf_nxt)[2][2],
+                                            const LdsFrags& fn, int nslab) {
+  constexpr int A = 0, B = 1;
+  auto rescore = [&](int qb) {
+    return [&, qb](float (&sv)[16]) {
+      f32x16 s = {};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) s = qk_one(s, fr.k(slab, kk), qf[qb][kk]);
+      scores_of_impl<kMasked>(sv, s, slab, last[qb]);
+    };
+  };
+  f32x16 sa = {}, sb = {};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) sa = qk_one(sa, kf[kk], qf[A][kk]);
+  float sva[16], svb[16];
+  unsigned pwa[8], pwb[8];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    sb = qk_one(sb, kf[kk], qf[B][kk]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kk == 0) {
+      scores_of_impl<kMasked>(sva, sa, slab, last[A]);
+      if (kFirst) first_reference(st[A], sva, c);
+    }
+    slab_weights<kMasked>(sva, pwa, st[A].mc, c, 2 * kk, 2 * kk + 2);
+    if (kk == 1) {  // the next slab's K fragments (this slab's are used by the MFMAs above)
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) kf_nxt[k2] = fn.k(nslab, k2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float psa = slab_rowsum(pwa, sel);
+  scores_of_impl<kMasked>(svb, sb, slab, last[B]);
+  if (kFirst) first_reference(st[B], svb, c);
+  slab_weights<kMasked>(svb, pwb, st[B].mc, c, 0, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  check_reference<kMasked>(st[A], rescore(A), pwa, psa, c, sel);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pv_one(st[A], vf[j >> 1][j & 1], pwa, j >> 1, j & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < 3) slab_weights<kMasked>(svb, pwb, st[B].mc, c, 2 * j + 2, 2 * j + 4);
+    if (j == 1) {  // the next slab's V fragments go to the other register set
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) vf_nxt[jj][blk] = fn.v(nslab, jj, blk);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float psb = slab_rowsum(pwb, sel);
+  check_reference<kMasked>(st[B], rescore(B), pwb, psb, c, sel);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pv_one(st[B], vf[j >> 1][j & 1], pwb, j >> 1, j & 1);
+}
+
+template <bool kCausal>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r64(AttnArgs a, float c, unsigned q_sign, int n_qblk) {
+  constexpr int kRowsPerWave = 64;
+  constexpr int kRows = 256;
+  __shared__ __attribute__((aligned(16))) char smem[kNStages * kStageBytes];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lq = lane & 31;
+  const int hf = lane >> 5;
+  const int n_q = a.n_q;
+  const bf16x8 sel = rowsum_selector(lane);
+
+  int bh, qblk;
+  if (kCausal) {
+    // heaviest query blocks (most key tiles) are dispatched first; workgroup i
+    // goes to XCD i % 8, so XCD x takes the heads bh = x (mod 8) and all of a
+    // head's query blocks share one L2
+    const int BH = a.batch * a.heads;
+    if ((BH & 7) == 0) {
+      const int x = blockIdx.x & 7, j = blockIdx.x >> 3, bhx = BH >> 3;
+      qblk = n_qblk - 1 - j / bhx;
+      bh = x + 8 * (j % bhx);
+    } else {
+      qblk = n_qblk - 1 - (int)(blockIdx.x / BH);
+      bh = (int)(blockIdx.x % BH);
+    }
+  } else {
+    const int total = gridDim.x, id = blockIdx.x;
+    const int per = total >> 3, rem = total & 7, x = id & 7, slot = id >> 3;
+    const int logical = (x < rem) ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
+    bh = logical / n_qblk;
+    qblk = logical - bh * n_qblk;
+  }
+  const int b_ = bh / a.heads, h_ = bh - b_ * a.heads;
+  const int n_k = a.kv_len != nullptr ? min(max(a.kv_len[b_], 0), a.n_k) : a.n_k;
+  const bf16* qp = static_cast<const bf16*>(a.q) + b_ * a.q_sb + h_ * a.q_sh;
+  const bf16* kp = static_cast<const bf16*>(a.k) + b_ * a.k_sb + h_ * a.k_sh;
+  const bf16* vp = static_cast<const bf16*>(a.v) + b_ * a.v_sb + h_ * a.v_sh;
+  bf16* op = static_cast<bf16*>(a.o) + b_ * a.o_sb + h_ * a.o_sh;
+  const int q_wave0 = qblk * kRows + wave * kRowsPerWave;
+
+  u32x4 qf[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_q = q_wave0 + 32 * qb + lq;
+    const bf16* src = qp + (int64_t)min(my_q, n_q - 1) * a.q_sn + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = my_q < n_q ? (ld16(src + 16 * kk) ^ q_sign) : u32x4{0, 0, 0, 0};
+  }
+  const int kv_end = kCausal ? min(n_k, qblk * kRows + kRows) : n_k;
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto dma_tile = [&](int tile) {
+    const int k0 = tile * kBN;
+    const int valid = min(n_k - k0, kBN);
+    const unsigned long long kb = (unsigned long long)(kp + (int64_t)k0 * a.k_sn);
+    const unsigned long long vb = (unsigned long long)(vp + (int64_t)k0 * a.v_sn);
+    auto uni = [](unsigned x) { return (unsigned)__builtin_amdgcn_readfirstlane((int)x); };
+    const u32x4 kr = {uni((unsigned)kb), uni((unsigned)(kb >> 32) & 0xffffu),
+                      uni(valid > 0 ? (unsigned)((valid - 1) * a.k_sn * 2 + 2 * 64) : 0u), (unsigned)kBufferFlags};
+    const u32x4 vr = {uni((unsigned)vb), uni((unsigned)(vb >> 32) & 0xffffu),
+                      uni(valid > 0 ? (unsigned)((valid - 1) * a.v_sn * 2 + 2 * 64) : 0u), (unsigned)kBufferFlags};
+    const unsigned st_base = uni(lds_off(smem) + (unsigned)((tile % kNStages) * kStageBytes));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int R = 16 * wave + 8 * i + (lane >> 3);
+      const int cch = (lane & 7) ^ (lane >> 3);
+      const int kr5 = R & 31;
+      const int key_k = (R & 32) | (kr5 & ~12) | ((kr5 >> 1) & 4) | ((kr5 << 1) & 8);
+      dma16(kr, (key_k * (int)a.k_sn + 8 * cch) * 2, st_base + (unsigned)((16 * wave_u + 8 * i) * kRowBytes));
+      dma16(vr, (R * (int)a.v_sn + 8 * cch) * 2, st_base + (unsigned)(64 * kRowBytes + (16 * wave_u + 8 * i) * kRowBytes));
+    }
+  };
+  LdsFrags fr0;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) fr0.klane[kk] = lq * kRowBytes + 16 * ((2 * kk + hf) ^ (lq & 7));
+  {
+    const int g = lane >> 4, j = lane & 15;
+    const int c_lane = 2 * (g & 1) + ((j & 3) >> 1);
+    fr0.vlane = (8 * (g >> 1) + (j >> 2)) * kRowBytes + 16 * (c_lane ^ (j >> 2)) + 8 * (j & 1);
+  }
+  fr0.base = smem;
+  auto frags_of = [&](int t) {
+    LdsFrags f = fr0;
+    f.base = smem + (t % kNStages) * kStageBytes;
+    return f;
+  };
+  auto tile_sync = [&](int t) {
+    if (t + 2 < ntiles)
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 3 < ntiles) dma_tile(t + 3);
+  };
+
+  RowState st[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    st[qb].o0 = f32x16{};
+    st[qb].o1 = f32x16{};
+    st[qb].m = -INFINITY;
+    st[qb].mc = 0.f;
+    st[qb].l = 0.f;
+  }
+  if (ntiles > 0) dma_tile(0);
+  if (ntiles > 1) dma_tile(1);
+  if (ntiles > 2) dma_tile(2);
+
+  // fragments: set 0 for slab 0 of a tile, set 1 for slab 1
+  u32x4 kf0[4], kf1[4], vf0[2][2], vf1[2][2];
+  if (ntiles > 0) {
+    tile_sync(0);
+    const LdsFrags f = frags_of(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf0[kk] = f.k(0, kk);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) vf0[jj][blk] = f.v(0, jj, blk);
+  }
+  const int t_split = min(kCausal ? qblk * (kRows / kBN) : ntiles, n_k / kBN);
+  const int no_mask[2] = {};
+  auto tile = [&](auto masked, auto first, int t) {
+    constexpr bool kM = decltype(masked)::value, kF = decltype(first)::value;
+    const int k0 = t * kBN;
+    int last[2] = {0, 0};
+    if (kM) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        last[qb] = (kCausal ? min(n_k - 1, q_wave0 + 32 * qb + lq) : n_k - 1) - k0 - 8 * hf;
+    }
+    const LdsFrags fc = frags_of(t);
+    // slab 1 reads the next tile's slab-0 fragments (this tile's again on the last)
+    const LdsFrags fn = frags_of(t + 1 < ntiles ? t + 1 : t);
+    attend_slab<kM, kF>(st, qf, fc, 0, kM ? last : no_mask, c, sel, kf0, vf0, kf1, vf1, fc, 1);
+    attend_slab<kM, false>(st, qf, fc, 1, kM ? last : no_mask, c, sel, kf1, vf1, kf0, vf0, fn, 0);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  int t = 0;
+  if (t_split > 0) {
+    tile(F{}, T{}, 0);
+    if (1 < ntiles) tile_sync(1);
+    t = 1;
+  }
+  for (; t < t_split; ++t) {
+    tile(F{}, F{}, t);
+    if (t + 1 < ntiles) tile_sync(t + 1);
+  }
+  for (; t < ntiles; ++t) {
+    const int k0 = t * kBN;
+    if (!kCausal || k0 <= q_wave0 + kRowsPerWave - 1) tile(T{}, F{}, t);  // wave-uniform
+    if (t + 1 < ntiles) tile_sync(t + 1);
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_q = q_wave0 + 32 * qb + lq;
+    const float l_tot = st[qb].l;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    unsigned w[2][4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      w[0][g][0] = pack_bf16(st[qb].o0[4 * g] * inv, st[qb].o0[4 * g + 1] * inv);
+      w[0][g][1] = pack_bf16(st[qb].o0[4 * g + 2] * inv, st[qb].o0[4 * g + 3] * inv);
+      w[1][g][0] = pack_bf16(st[qb].o1[4 * g] * inv, st[qb].o1[4 * g + 1] * inv);
+      w[1][g][1] = pack_bf16(st[qb].o1[4 * g + 2] * inv, st[qb].o1[4 * g + 3] * inv);
+    }
+    u32x4 chunk[2][2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        chunk[blk][tt] =
+            gather_row_chunk(w[blk][2 * tt][0], w[blk][2 * tt][1], w[blk][2 * tt + 1][0], w[blk][2 * tt + 1][1]);
+    if (my_q < n_q) {
+      bf16* dst = op + (int64_t)my_q * a.o_sn;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          *reinterpret_cast<u32x4*>(dst + 32 * blk + 8 * (2 * tt + hf)) = chunk[blk][tt];
+      if (a.lse != nullptr && hf == 0)
+        a.lse[(int64_t)bh * n_q + my_q] = l_tot > 0.f ? (st[qb].mc + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+static void launch_slab(const AttnArgs& a, hipStream_t stream, float c, unsigned q_sign) {
+  const int n_qblk = (a.n_q + 255) / 256;
+  const dim3 grid((unsigned)(n_qblk * a.batch * a.heads));
+  if (a.causal)
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r64<true>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r64<false>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+}
+
 }  // namespace
 
-// Rows per wavefront: 64 (two 32-row blocks share every K/V fragment read)
-// in 256-row workgroups, else 32. Measured on MI355X: 64 rows pay off for
-// long query runs with little padding (longer K/V streams per workgroup) and
-// for unmasked runs that fill whole 256-row workgroups (the encoder launch,
-// 29 -> 27 us at N = 512); for short causal or ragged runs the 32-row form's
-// finer split wins.
+// Rows per wavefront: 64 (two 32-row blocks share every K/V fragment read;
+// the slab-prefetching kernel) in 256-row workgroups, else 32. Measured on
+// MI355X: 64 rows pay off for long query runs with little padding (longer K/V
+// streams per workgroup) and for unmasked runs that fill whole 256-row
+// workgroups (the encoder launch); for short causal or ragged runs the 32-row
+// form's occupancy and finer causal split win.
 int attention_rows_per_wave(int n_q, bool causal) {
   const int pad256 = (n_q + 255) / 256 * 256 - n_q;
   if (!causal && n_q >= 512 && pad256 == 0) return 64;
   return (n_q >= 2048 && pad256 * 16 <= n_q) ? 64 : 32;
 }
 
-template <int kQB>
-static void launch_qb(const AttnArgs& a, hipStream_t stream, float c, unsigned q_sign) {
-  const int rows = 4 * 32 * kQB;
-  const int n_qblk = (a.n_q + rows - 1) / rows;
+static void launch_rows32(const AttnArgs& a, hipStream_t stream, float c, unsigned q_sign) {
+  const int n_qblk = (a.n_q + 127) / 128;
   const dim3 grid((unsigned)(n_qblk * a.batch * a.heads));
   if (a.causal)
-    hipLaunchKernelGGL((attn_fwd_bf16_d64<true, kQB>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r32<true>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_d64<false, kQB>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r32<false>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
 }
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
@@ -579,9 +837,9 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
   const float c = fabsf(a.scale) * kLog2e;
   const unsigned q_sign = a.scale < 0.f ? 0x80008000u : 0u;  // negate Q exactly: scale*s = |scale|*(-q).k
   if (attention_rows_per_wave(a.n_q, a.causal != 0) == 64)
-    launch_qb<2>(a, stream, c, q_sign);
+    launch_slab(a, stream, c, q_sign);
   else
-    launch_qb<1>(a, stream, c, q_sign);
+    launch_rows32(a, stream, c, q_sign);
   return hipGetLastError();
 }
 
