@@ -14,9 +14,9 @@ in float64, materialising the full score matrix:
   (worksonmygpu.com), "Scaled dot-product attention", steps 1-4.
 * MultiHead(Q, K, V) = Concat(head_1..head_h) W^O with
   head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V) -- same page, the MultiHead
-  equation; the split into h contiguous column blocks and the concat in head
-  order follow the multi_head snippet of "32 Transformer"
-  (ml-canon-en.vercel.app), "PyTorch Implementation".
+  equation and its symbol table, written out head by head: W_i is the i-th
+  block of d_k columns of the stored projection matrix, and Concat lays the
+  heads side by side in order.
 * The causal mask is an additive matrix, 0 on and below the diagonal and -inf
   above it, added to the scores before the softmax, so a blocked key gets a
   weight of exactly 0 -- "The Transformer" (rayaq.ca), "Masks: who may look at
@@ -300,34 +300,25 @@ def causal_mask_rows(n: int, rows) -> np.ndarray:
     return out
 
 
-def split_heads(t: np.ndarray, heads: int) -> np.ndarray:
-    """(B, N, h*d) -> (B, h, N, d): head i takes columns [i*d, (i+1)*d).
-
-    "32 Transformer", "PyTorch Implementation": view(seq, h, -1) then
-    transpose, per batch item.
-    """
-    B, N, D = t.shape
-    return t.reshape(B, N, heads, D // heads).transpose(0, 2, 1, 3)
-
-
-def concat_heads(t: np.ndarray) -> np.ndarray:
-    """(B, h, N, d) -> (B, N, h*d), heads side by side in order."""
-    B, H, N, d = t.shape
-    return t.transpose(0, 2, 1, 3).reshape(B, N, H * d)
-
-
 def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: np.ndarray,
             wv: np.ndarray, wo: np.ndarray, heads: int, *, causal: bool = False,
             rows=None, kv_len=None, bq=None, bk=None, bv=None, bo=None) -> np.ndarray:
-    """MultiHead(Xq, Xk, Xv) = Concat(head_1..head_h) W^O, no biases.
+    """MultiHead(Xq, Xk, Xv) = Concat(head_1, ..., head_h) W^O with
+    head_i = Attention(Xq W_i^Q, Xk W_i^K, Xv W_i^V).
+
+    "The Transformer" (hoshank.vercel.app), "The Mathematics": the MultiHead
+    equation and its symbol table (W_i^Q, W_i^K, W_i^V are d_model x d_k,
+    W^O is h d_v x d_model, d_k = d_v = d_model / h). Written out head by
+    head: W_i^Q is column block i of the stored (d_model, d_model) matrix
+    (head i owns columns [i d_k, (i + 1) d_k)), each head runs Attention on
+    its own projections, Concat lays head_1 .. head_h side by side in that
+    order, and the result is multiplied by W^O.
 
     xq: (B, N_q, d_model); xk, xv: (B, N_k, d_model); w*: (d_model, d_model)
-    stored (in, out). Scale is 1/sqrt(d_model / heads).
-    "The Transformer" (hoshank.vercel.app), "The Mathematics", MultiHead
-    equation; "32 Transformer", "PyTorch Implementation", multi_head.
-    Self-attention passes the same x three times; cross-attention passes the
-    decoder state as xq and the encoder memory as xk and xv ("The Transformer"
-    (rayaq.ca), "The decoder stack").
+    stored (in, out). Scale is 1/sqrt(d_model / heads). Self-attention passes
+    the same x three times; cross-attention passes the decoder state as xq and
+    the encoder memory as xk and xv ("The Transformer" (rayaq.ca), "The decoder
+    stack").
     rows: optional query positions; only those output rows are returned.
     kv_len: optional per-batch number of valid key/value positions of the
     xk/xv sequence (a key-padding mask, as in attention_ref).
@@ -342,15 +333,22 @@ def mha_ref(xq: np.ndarray, xk: np.ndarray, xv: np.ndarray, wq: np.ndarray, wk: 
     d_model = xq.shape[-1]
     if d_model % heads:
         raise ValueError("d_model must be divisible by the number of heads")
-    def proj(x, w, b):
-        y = np.matmul(x, np.asarray(w, dtype=np.float64))
-        return y if b is None else y + np.asarray(b, dtype=np.float64)
+    d = d_model // heads
 
-    q, k, v = proj(xq, wq, bq), proj(xk, wk, bk), proj(xv, wv, bv)
-    qh, kh, vh = split_heads(q, heads), split_heads(k, heads), split_heads(v, heads)
-    o, _, _ = attention_ref(qh, kh, vh, causal=causal, scale=1.0 / math.sqrt(d_model // heads),
-                            rows=rows, kv_len=kv_len)
-    return proj(concat_heads(o), wo, bo)
+    def proj(x, w, b, cols=slice(None)):
+        y = np.matmul(x, np.asarray(w, dtype=np.float64)[:, cols])
+        return y if b is None else y + np.asarray(b, dtype=np.float64)[cols]
+
+    head_outputs = []
+    for i in range(heads):
+        cols = slice(i * d, (i + 1) * d)
+        qi, ki, vi = proj(xq, wq, bq, cols), proj(xk, wk, bk, cols), proj(xv, wv, bv, cols)
+        # one head: attention_ref takes (B, H, N, d), here with H = 1
+        oi, _, _ = attention_ref(qi[:, None], ki[:, None], vi[:, None], causal=causal,
+                                 scale=1.0 / math.sqrt(d), rows=rows, kv_len=kv_len)
+        head_outputs.append(oi[:, 0])
+    concat = np.concatenate(head_outputs, axis=-1)  # head_1 in columns [0, d), then head_2, ...
+    return proj(concat, wo, bo)
 
 
 def layer_norm_ref(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float) -> np.ndarray:
