@@ -9,7 +9,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
+# MHA_LIBRARY points the binding at another build of the same C ABI (the
+# host AddressSanitizer build of the front end used by the CPU tests)
+LIB_PATH = os.environ.get("MHA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
 
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_WORKSPACE, MHA_ERR_HIP = range(5)
 MHA_F32, MHA_BF16 = 0, 1

@@ -84,5 +84,29 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_LIB = os.path.join(OBJDIR, "libmha_host_asan.so")
+
+
+def build_host_asan(verbose: bool = False) -> str:
+    """The C front end (mha_api.cpp: validation, workspace layout, status and
+    error text) built for the host with AddressSanitizer, its kernel launchers
+    replaced by stubs (tests/asan/launch_stubs.cpp). CPU only: no device code."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+           "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, "mha_api.cpp"),
+           os.path.join(ROOT, "tests", "asan", "launch_stubs.cpp"), "-L/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", ASAN_LIB]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("host ASan build failed:\n" + r.stdout + r.stderr)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -111,14 +111,14 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace mha
 
-// Defined in mha_api.cpp for entry points in other sources (they need the
-// status type of the public header).
+// Shared by the sources of the library's entry points (they need the status
+// type of the public header).
 #include "mha.h"
 namespace mha {
 mha_status report_error(mha_status s, const char* msg);
-mha_status mha_forward_on_workspace(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk,
-                                    const void* wv, const void* wo, void* out, void* workspace,
-                                    size_t workspace_bytes, int batch, int n_q, int n_k, int d_model, int heads,
-                                    mha_dtype dtype, int causal, void* stream);
+// Defined in noalloc.hip: the current device's fixed workspace array of
+// mha_forward_noalloc (its device address, looked up once per device) and
+// its size.
+mha_status noalloc_scratch(void** ptr, size_t* bytes);
 
 }  // namespace mha

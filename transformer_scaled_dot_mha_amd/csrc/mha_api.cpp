@@ -487,18 +487,8 @@ mha_status backward_impl(const void* q, const void* k, const void* v, const void
 }  // namespace
 
 namespace mha {
-// Entry points defined in other sources of the library use these two: the
-// thread-local error text, and mha_forward's body (with its validation) on a
-// workspace they supply.
+// The thread-local error text, for sources other than this one.
 mha_status report_error(mha_status s, const char* msg) { return fail(s, "%s", msg); }
-
-mha_status mha_forward_on_workspace(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk,
-                                    const void* wv, const void* wo, void* out, void* workspace,
-                                    size_t workspace_bytes, int batch, int n_q, int n_k, int d_model, int heads,
-                                    mha_dtype dtype, int causal, void* stream) {
-  return mha_impl(xq, xk, xv, wq, wk, wv, wo, out, workspace, workspace_bytes, batch, n_q, n_k, d_model, heads, dtype,
-                  causal, nullptr, stream);
-}
 }  // namespace mha
 
 extern "C" {
@@ -604,6 +594,33 @@ mha_status mha_forward(const void* xq, const void* xk, const void* xv, const voi
                     dtype, causal, nullptr, stream);
   } catch (...) {
     return fail(MHA_ERR_HIP, "internal error in mha_forward");
+  }
+}
+
+mha_status mha_forward_noalloc(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk,
+                               const void* wv, const void* wo, void* out, int batch, int n_q, int n_k, int d_model,
+                               int heads, mha_dtype dtype, int causal, void* stream) {
+  try {
+    // size checks first, before any HIP call
+    const size_t need = mha_forward_workspace_size(batch, n_q, n_k, d_model, heads, dtype);
+    if (need == 0) return fail(MHA_ERR_INVALID_ARG, "invalid sizes or dtype (the workspace size is undefined)");
+    if (need > MHA_NOALLOC_MAX_WORKSPACE)
+      return fail(MHA_ERR_UNSUPPORTED,
+                  "problem needs a %zu-byte workspace, more than mha_forward_noalloc's fixed 128 MiB; call "
+                  "mha_forward with a workspace instead",
+                  need);
+    // the rest of mha_forward's validation runs before its first launch; only
+    // the lookup of this device's array precedes it, so reject bad pointers first
+    if (!xq || !xk || !xv || !wq || !wk || !wv || !wo || !out)
+      return fail(MHA_ERR_INVALID_ARG, "inputs, weights and out must be non-null");
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    const mha_status s = mha::noalloc_scratch(&ws, &ws_bytes);
+    if (s != MHA_OK) return s;
+    return mha_impl(xq, xk, xv, wq, wk, wv, wo, out, ws, ws_bytes, batch, n_q, n_k, d_model, heads, dtype, causal,
+                    nullptr, stream);
+  } catch (...) {
+    return fail(MHA_ERR_HIP, "internal error in mha_forward_noalloc");
   }
 }
 

@@ -1,6 +1,7 @@
-// mha_forward without a caller-supplied workspace, for callers that cannot
-// allocate device memory (code under HIP graph capture, tight serving loops,
-// harnesses that forbid allocation).
+// The workspace of mha_forward_noalloc (defined with the other entry points in
+// mha_api.cpp): mha_forward for callers that cannot allocate device memory
+// (code under HIP graph capture, tight serving loops, harnesses that forbid
+// allocation).
 //
 // mha_forward keeps its Q, K, V and concatenated-head intermediates in a
 // workspace. Here that workspace is a file-scope device array, `scratch`, of
@@ -53,32 +54,14 @@ mha_status scratch_of_current_device(void** out) {
 
 }  // namespace
 
-extern "C" {
+namespace mha {
 
-mha_status mha_forward_noalloc(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk,
-                               const void* wv, const void* wo, void* out, int batch, int n_q, int n_k, int d_model,
-                               int heads, mha_dtype dtype, int causal, void* stream) {
-  try {
-    // size checks first, before any HIP call
-    const size_t need = mha_forward_workspace_size(batch, n_q, n_k, d_model, heads, dtype);
-    if (need == 0)
-      return mha::report_error(MHA_ERR_INVALID_ARG, "invalid sizes or dtype (the workspace size is undefined)");
-    if (need > kScratchBytes)
-      return mha::report_error(MHA_ERR_UNSUPPORTED,
-                               "problem needs a larger workspace than mha_forward_noalloc's fixed 128 MiB; "
-                               "call mha_forward with a workspace instead");
-    // the rest of mha_forward's validation runs before its first launch; only
-    // the lookup of this device's array precedes it, so reject bad pointers first
-    if (!xq || !xk || !xv || !wq || !wk || !wv || !wo || !out)
-      return mha::report_error(MHA_ERR_INVALID_ARG, "inputs, weights and out must be non-null");
-    void* ws = nullptr;
-    mha_status s = scratch_of_current_device(&ws);
-    if (s != MHA_OK) return s;
-    return mha::mha_forward_on_workspace(xq, xk, xv, wq, wk, wv, wo, out, ws, kScratchBytes, batch, n_q, n_k,
-                                         d_model, heads, dtype, causal, stream);
-  } catch (...) {
-    return mha::report_error(MHA_ERR_HIP, "internal error in mha_forward_noalloc");
-  }
+// The current device's copy of `scratch` and its size (for
+// mha_forward_noalloc in mha_api.cpp).
+mha_status noalloc_scratch(void** ptr, size_t* bytes) {
+  mha_status s = scratch_of_current_device(ptr);
+  *bytes = kScratchBytes;
+  return s;
 }
 
-}  // extern "C"
+}  // namespace mha
