@@ -15,11 +15,12 @@
 // slice of X^T, and each lane ends with 4 consecutive columns of one row.
 //
 // Staging: 32-deep k chunks go straight from global memory into LDS with
-// buffer loads that write LDS (no staging registers, no VALU), into a ring of
-// three stages, two chunks ahead of the one being multiplied; one barrier per
-// chunk. The loads are issued from inline asm and awaited with explicit vmcnt
-// waits, so that the compiler does not wait for every outstanding chunk before
-// each LDS read. X rows keep their layout (64-byte rows, the 16-byte chunk c
+// buffer loads that write LDS (no staging registers, no VALU), into two
+// stages: chunk c + 1 loads while chunk c is multiplied; one barrier per
+// chunk. Two stages keep the 128-row tile at 32 KB of LDS, so five workgroups
+// share a CU (96 VGPRs), and more resident workgroups hide the load latency
+// better than a deeper ring with fewer of them. The loads are issued from
+// inline asm and awaited with explicit vmcnt waits. X rows keep their layout (64-byte rows, the 16-byte chunk c
 // of row r stored at position c ^ ((r >> 2) & 3), so that the 16-byte
 // fragment reads of 16 consecutive rows hit distinct banks); W rows keep
 // theirs (256-byte rows, chunk c of k-row r at c ^ (r & 15)) and the W^T
@@ -33,7 +34,7 @@
 // from HBM once. The tile height is the one whose workgroup count fills whole
 // rounds of 512 workgroups best, 128 on ties: at these sizes the kernel is
 // bound by load latency rather than by the matrix cores, and the smaller tile
-// keeps more workgroups in flight (three per CU against two for the 256-row
+// keeps more workgroups in flight (five per CU against two for the 256-row
 // tile, by LDS).
 #include <hip/hip_runtime.h>
 
@@ -54,7 +55,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int kTN = 128, kTK = 32;
 constexpr int kXRow = kTK * 2;  // 64-byte X rows in LDS (one k chunk of an m row)
 constexpr int kWRow = kTN * 2;  // 256-byte W rows in LDS (the tile's n columns of a k row)
-constexpr int kNStages = 3;     // LDS ring: chunk c is read while c + 1 and c + 2 load
+constexpr int kNStages = 2;     // LDS stages: chunk c is read while c + 1 loads
 constexpr int kBufferFlags = 0x00020000;       // raw buffer descriptor word 3 (gfx9 family: 32-bit data format)
 constexpr unsigned kOutOfRange = 0x80000000u;  // byte offset past any record count: the load returns zero
 
@@ -100,7 +101,9 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
   constexpr int kStageBytes = kXBytes + kTK * kWRow;
   constexpr int kXDma = kTM / 64;  // X loads per wavefront per chunk (16 rows of 64 B each)
   constexpr int kWDma = 2;         // W loads per wavefront per chunk (4 rows of 256 B each)
-  __shared__ __attribute__((aligned(16))) char smem[kNStages * kStageBytes];
+  // the stages, and afterwards the output tile (kTM rows of 256 bytes)
+  constexpr int kSmem = kNStages * kStageBytes > kTM * kWRow ? kNStages * kStageBytes : kTM * kWRow;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   const int n = args.n, kdim = args.k, groups = args.groups;
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; each XCD
@@ -209,25 +212,26 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
     }
   };
 
-  // Chunk c: wait for its loads (the next chunk's may stay in flight), barrier
-  // (which also ends every read of the stage chunk c + 2 reuses), start the
-  // loads of chunk c + 2, multiply.
+  // Chunk c: wait for its loads, barrier (which also ends every read of the
+  // stage chunk c + 1 reuses), start the loads of chunk c + 1, multiply.
   const int nchunks = (kdim + kTK - 1) / kTK;
   dma_chunk(0);
-  if (nchunks > 1) dma_chunk(1);
   for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kXDma + kWDma) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (c + 2 < nchunks) dma_chunk(c + 2);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + 1 < nchunks) dma_chunk(c + 1);
     compute(c);
   }
 
-  // lane holds row wrow + 32*mb + lq and columns wcol + 32*nb + 8*q + 4*hf + 0..3;
-  // the two halves swap groups so that each lane writes 16-byte row chunks.
-  // Optional epilogue: + bias[column], then max(0, .), in fp32 before rounding.
+  // Epilogue. A lane holds row wrow + 32*mb + lq and columns wcol + 32*nb +
+  // 8*q + 4*hf + 0..3; the two halves swap groups so that each lane has whole
+  // 16-byte row chunks. Optional: + bias[column], then max(0, .), in fp32
+  // before rounding. The tile goes through LDS (the stages are free by now:
+  // kTM rows of 256 bytes, chunk c of row r at c ^ (r & 15), conflict-free
+  // both ways) so that the global stores write whole rows: 16 lanes per
+  // 256-byte row, where the accumulator layout would have each store
+  // instruction touch 32 rows with 32 bytes each.
   const bf16* Bias = static_cast<const bf16*>(g.bias);
+  __syncthreads();  // every wavefront is done reading the stages
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int row = wrow + 32 * mb + lq;
@@ -260,10 +264,20 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const u32x4 chunk = gather_row_chunk(w[2 * t][0], w[2 * t][1], w[2 * t + 1][0], w[2 * t + 1][1]);
-        const int col = wcol + 32 * nb + 16 * t + 8 * hf;
-        if (row < valid_m && col < valid_n)
-          *reinterpret_cast<u32x4*>(Y + (int64_t)(m0 + row) * g.ldy + n0 + col) = chunk;
+        const int c = (wcol + 32 * nb + 16 * t + 8 * hf) >> 3;
+        *reinterpret_cast<u32x4*>(smem + row * kWRow + 16 * (c ^ (row & 15))) = chunk;
       }
+    }
+  }
+  __syncthreads();
+  {
+    const int c = tid & 15;
+#pragma unroll
+    for (int i = 0; i < kTM / 16; ++i) {
+      const int r = (tid >> 4) + 16 * i;
+      if (r < valid_m && 8 * c < valid_n)
+        *reinterpret_cast<u32x4*>(Y + (int64_t)(m0 + r) * g.ldy + n0 + 8 * c) =
+            *reinterpret_cast<const u32x4*>(smem + r * kWRow + 16 * (c ^ (r & 15)));
     }
   }
 }
@@ -274,8 +288,8 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream) {
   for (int i = 0; i < a.groups; ++i) max_m = a.g[i].m > max_m ? a.g[i].m : max_m;
   const int tiles_n = (a.n + kTN - 1) / kTN;
   // the tile height whose workgroup count fills whole rounds of 512 best (the
-  // 256-row tile's residency, two per CU; the 128-row tile, 48 KB of LDS,
-  // fits three); ties go to the 128-row tile
+  // 256-row tile's residency, two per CU by its 64 KB of LDS; the 128-row
+  // tile, 32 KB, fits five); ties go to the 128-row tile
   const int64_t big = (int64_t)tiles_n * ((max_m + 255) / 256) * a.groups;
   const int64_t small = (int64_t)tiles_n * ((max_m + 127) / 128) * a.groups;
   auto fill = [](int64_t wgs) { return (double)wgs / (double)(((wgs + 511) / 512) * 512); };
