@@ -278,8 +278,13 @@ LINEAR_CASES = [
     (1000, 1536, 512, "bf16"), (64, 128, 1040, "bf16"), (16384, 512, 512, "bf16"),
     # 256-row tiles: 512 workgroups fill whole rounds, with ragged m and a partial last k chunk
     (8000, 2048, 520, "bf16"), (32513, 512, 512, "bf16"), (32640, 512, 512, "bf16"),
-    (37, 20, 12, "f32"), (129, 512, 512, "f32"),
+    # fp32: split-k form (small grids; k quarters of 16, 48 and 64 with a ragged last one), and the 64 x 64 form
+    (37, 20, 12, "f32"), (129, 512, 512, "f32"), (70, 136, 200, "f32"), (3, 4, 260, "f32"), (1100, 1040, 72, "f32"),
 ]
+
+
+def _linear_f32_form(m, n, groups=1):
+    return "split-k" if ((n + 63) // 64) * ((m + 63) // 64) * groups < 256 else "64x64"
 
 
 @pytest.mark.parametrize("m,n,k,dtype", LINEAR_CASES)
@@ -294,9 +299,10 @@ def test_linear_parity(dev, m, n, k, dtype):
 
 
 def test_linear_cases_reach_both_tile_heights():
-    """The case list above selects both bf16 tile forms (a host-side check of the list)."""
+    """The case list above selects both bf16 tile forms and both fp32 forms (a host-side check of the list)."""
     heights = {_linear_tile_rows(m, n) for m, n, k, dt in LINEAR_CASES if dt == "bf16"}
     assert heights == {128, 256}
+    assert {_linear_f32_form(m, n) for m, n, k, dt in LINEAR_CASES if dt == "f32"} == {"split-k", "64x64"}
 
 
 def test_mha_with_256_row_projection_tiles(dev):

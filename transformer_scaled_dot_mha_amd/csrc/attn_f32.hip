@@ -4,9 +4,16 @@
 // Transformer" (hoshank.vercel.app), "The Mathematics", Attention equation),
 // computed exactly in one pass over key tiles with a running row maximum and
 // row sum. This is the full-precision path (fp32 storage, fp32 products and
-// accumulation, no reduced-precision matrix modes) used by the fp32 workloads;
-// one thread owns one query row, and 32-key tiles of K and V are staged in
-// LDS and read by every thread of the workgroup (broadcast reads).
+// accumulation, no reduced-precision matrix modes) used by the fp32 workloads.
+//
+// A workgroup of 4 wavefronts owns 16 query rows of one (batch, head); four
+// lanes share a row, each holding a quarter of its d values (the partial dot
+// products are summed across the four lanes with DPP quad permutes). The
+// wavefronts split the key tiles between them (tile i goes to wavefront
+// i % 4), each staging its own tiles in its own LDS region, and the four
+// partial (max, sum, O) states of a row are merged at the end. Small problems
+// (a single 128-token sequence) then run on many wavefronts instead of a few
+// long serial loops.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -15,14 +22,24 @@
 namespace mha {
 namespace {
 
-constexpr int kRows = 64;  // query rows per workgroup (one wavefront)
-constexpr int kKeys = 32;  // keys per tile
+constexpr int kRows = 16;  // query rows per workgroup (four lanes per row, four wavefronts)
+
+// x summed over the four lanes of its quad (DPP quad permutes 1,0,3,2 and 2,3,0,1)
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  return x;
+}
 
 template <int D, bool kCausal>
-__global__ __launch_bounds__(kRows) void attn_fwd_f32(AttnArgs a, float c, float q_sign, int n_qblk) {
-  __shared__ float Ks[kKeys][D];
-  __shared__ float Vs[kKeys][D];
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(256) void attn_fwd_f32(AttnArgs a, float c, float q_sign, int n_qblk) {
+  constexpr int kKeys = D <= 64 ? 32 : 16;  // keys per tile
+  constexpr int kPart = D / 4;              // d values per lane
+  constexpr int kTile = kKeys * D;          // floats per K (or V) tile
+  static_assert(4 * 16 * (D + 2) <= 4 * 2 * kTile, "the merge fits in the tiles' LDS");
+  __shared__ __attribute__((aligned(16))) float smem[4 * 2 * kTile];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane >> 2, part = lane & 3;
   const int bh = blockIdx.x / n_qblk;
   const int qb = blockIdx.x - bh * n_qblk;
   const int b = bh / a.heads, h = bh - b * a.heads;
@@ -33,33 +50,50 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32(AttnArgs a, float c, float
   const int n_q = a.n_q;
   // keys visible to this batch item: all n_k, or its padded length
   const int n_k = a.kv_len != nullptr ? min(max(a.kv_len[b], 0), a.n_k) : a.n_k;
-  const int my_q = qb * kRows + tid;
+  const int q0 = qb * kRows;
+  const int my_q = q0 + r;
 
-  float qr[D], acc[D];
+  float q[kPart], acc[kPart];
 #pragma unroll
-  for (int t = 0; t < D; ++t) {
-    qr[t] = my_q < n_q ? q_sign * qp[(int64_t)my_q * a.q_sn + t] : 0.f;
-    acc[t] = 0.f;
+  for (int t = 0; t < kPart; t += 4) {
+    const float4 v = my_q < n_q ? *reinterpret_cast<const float4*>(qp + (int64_t)my_q * a.q_sn + part * kPart + t)
+                                : float4{0.f, 0.f, 0.f, 0.f};
+    q[t] = q_sign * v.x;
+    q[t + 1] = q_sign * v.y;
+    q[t + 2] = q_sign * v.z;
+    q[t + 3] = q_sign * v.w;
   }
+#pragma unroll
+  for (int t = 0; t < kPart; ++t) acc[t] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const int kv_end = kCausal ? min(n_k, qb * kRows + kRows) : n_k;
+  const int kv_end = kCausal ? min(n_k, q0 + kRows) : n_k;
+  const int ntile = (kv_end + kKeys - 1) / kKeys;
+  float* Ks = smem + wave * 2 * kTile;
+  float* Vs = Ks + kTile;
 
-  for (int k0 = 0; k0 < kv_end; k0 += kKeys) {
-    __syncthreads();
-    for (int idx = tid; idx < kKeys * D; idx += kRows) {
-      const int r = idx / D, col = idx - r * D;
-      const int key = k0 + r;
-      Ks[r][col] = key < n_k ? kp[(int64_t)key * a.k_sn + col] : 0.f;
-      Vs[r][col] = key < n_k ? vp[(int64_t)key * a.v_sn + col] : 0.f;
+  for (int ti = wave; ti < ntile; ti += 4) {  // wave-uniform
+    const int k0 = ti * kKeys;
+    // this wavefront's tile (only its own lanes read it, so no barrier)
+#pragma unroll
+    for (int i = lane; i < kTile / 4; i += 64) {
+      const int key = i / (D / 4), c4 = 4 * (i - key * (D / 4));
+      const bool in = k0 + key < n_k;
+      const float4 kv = in ? *reinterpret_cast<const float4*>(kp + (int64_t)(k0 + key) * a.k_sn + c4)
+                           : float4{0.f, 0.f, 0.f, 0.f};
+      const float4 vv = in ? *reinterpret_cast<const float4*>(vp + (int64_t)(k0 + key) * a.v_sn + c4)
+                           : float4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<float4*>(Ks + key * D + c4) = kv;
+      *reinterpret_cast<float4*>(Vs + key * D + c4) = vv;
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     float s[kKeys];
     float tmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kKeys; ++j) {
       float dot = 0.f;
 #pragma unroll
-      for (int t = 0; t < D; ++t) dot = fmaf(qr[t], Ks[j][t], dot);
+      for (int t = 0; t < kPart; ++t) dot = fmaf(q[t], Ks[j * D + part * kPart + t], dot);
+      dot = quad_sum(dot);
       const int key = k0 + j;
       const bool ok = key < n_k && (!kCausal || key <= my_q);
       s[j] = ok ? dot : -INFINITY;
@@ -71,23 +105,58 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32(AttnArgs a, float c, float
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
-    for (int t = 0; t < D; ++t) acc[t] *= alpha;
+    for (int t = 0; t < kPart; ++t) acc[t] *= alpha;
 #pragma unroll
     for (int j = 0; j < kKeys; ++j) {
       const float p = s[j] == -INFINITY ? 0.f : exp2f(fmaf(s[j], c, -mc));
       l_run += p;
 #pragma unroll
-      for (int t = 0; t < D; ++t) acc[t] = fmaf(p, Vs[j][t], acc[t]);
+      for (int t = 0; t < kPart; ++t) acc[t] = fmaf(p, Vs[j * D + part * kPart + t], acc[t]);
     }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // reads done before the next tile's writes
   }
-  if (my_q < n_q) {
-    // a row with no visible key (padded length 0) has l = 0: output 0, lse -inf
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    float* dst = op + (int64_t)my_q * a.o_sn;
+
+  // merge the four wavefronts' states of each row: [wave][row][D + 2]
+  __syncthreads();
+  float* red = smem + (wave * kRows + r) * (D + 2);
 #pragma unroll
-    for (int t = 0; t < D; ++t) dst[t] = acc[t] * inv;
-    if (a.lse != nullptr)
-      a.lse[(int64_t)bh * n_q + my_q] = l_run > 0.f ? m_run * (c / 1.4426950408889634f) + logf(l_run) : -INFINITY;
+  for (int t = 0; t < kPart; ++t) red[part * kPart + t] = acc[t];
+  if (part == 0) {
+    red[D] = m_run;
+    red[D + 1] = l_run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float mw[4], lw[4], m_all = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* rw = smem + (w * kRows + r) * (D + 2);
+      mw[w] = rw[D];
+      lw[w] = rw[D + 1];
+      m_all = fmaxf(m_all, mw[w]);
+    }
+    const float mc = (m_all == -INFINITY ? 0.f : m_all) * c;
+    float wt[4], l_all = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wt[w] = mw[w] == -INFINITY ? 0.f : exp2f(fmaf(mw[w], c, -mc));
+      l_all = fmaf(wt[w], lw[w], l_all);
+    }
+    if (my_q < n_q) {
+      // a row with no visible key (padded length 0) has l = 0: output 0, lse -inf
+      const float inv = l_all > 0.f ? 1.0f / l_all : 0.f;
+      float* dst = op + (int64_t)my_q * a.o_sn + part * kPart;
+#pragma unroll
+      for (int t = 0; t < kPart; ++t) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o = fmaf(wt[w], smem[(w * kRows + r) * (D + 2) + part * kPart + t], o);
+        dst[t] = o * inv;
+      }
+      if (a.lse != nullptr && part == 0)
+        a.lse[(int64_t)bh * n_q + my_q] =
+            l_all > 0.f ? m_all * (c / 1.4426950408889634f) + logf(l_all) : -INFINITY;
+    }
   }
 }
 
@@ -98,9 +167,9 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   const int n_qblk = (a.n_q + kRows - 1) / kRows;
   const dim3 grid((unsigned)(n_qblk * a.batch * a.heads));
   if (a.causal)
-    hipLaunchKernelGGL((attn_fwd_f32<D, true>), grid, dim3(kRows), 0, stream, a, c, q_sign, n_qblk);
+    hipLaunchKernelGGL((attn_fwd_f32<D, true>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
   else
-    hipLaunchKernelGGL((attn_fwd_f32<D, false>), grid, dim3(kRows), 0, stream, a, c, q_sign, n_qblk);
+    hipLaunchKernelGGL((attn_fwd_f32<D, false>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
   return hipGetLastError();
 }
 

@@ -6,6 +6,12 @@
 // MultiHead equation). 64 x 64 output tile per workgroup of 256 threads, each
 // thread 4 x 4 outputs, 16-deep k steps staged through LDS. Optional epilogue:
 // a bias per column and a ReLU (the FFN's max(0, x W1 + b1)).
+//
+// Grids of fewer than 256 such tiles (a single short sequence) take a second
+// form instead: 32 x 32 tiles whose four wavefronts each run a quarter of k
+// (their own LDS chunks, the next chunk's loads in flight in registers), the
+// four partial tiles summed at the end, so that short problems spread over
+// many wavefronts instead of long serial k loops.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -71,6 +77,84 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(LinearArgs args, int ti
   }
 }
 
+
+// 32 x 32 output tile; wavefront w runs k range [w kq, (w + 1) kq) in
+// 16-deep chunks staged in its own LDS region; lane (ty, tx) = (lane / 8,
+// lane % 8) accumulates rows 4 ty.., columns 4 tx..
+__global__ __launch_bounds__(256) void linear_f32_splitk(LinearArgs args, int tiles_n) {
+  constexpr int kS = 32, kC = 16;
+  __shared__ float Xs[4][kC][kS + 4];
+  __shared__ float Ws[4][kC][kS];
+  __shared__ float red[4][kS][kS + 1];
+  const LinearGroup g = blockIdx.y == 0 ? args.g[0] : (blockIdx.y == 1 ? args.g[1] : args.g[2]);
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int m0 = tm * kS, n0 = tn * kS;
+  if (m0 >= g.m) return;  // workgroup-uniform
+  const int n = args.n, kdim = args.k;
+  const float* X = static_cast<const float*>(g.x);
+  const float* W = static_cast<const float*>(g.w);
+  float* Y = static_cast<float*>(g.y);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, tx = lane & 7, ty = lane >> 3;
+  const int kq = (kdim + 4 * kC - 1) / (4 * kC) * kC;  // each wavefront's k range, a multiple of 16
+  const int kb = w * kq, ke = min(kdim, kb + kq);
+  float xr[8], wr[8];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = lane + 64 * i;
+      const int r = idx >> 4, kk = idx & 15, row = m0 + r, col = k0 + kk;
+      xr[i] = (row < g.m && col < ke) ? X[(int64_t)row * g.ldx + col] : 0.f;
+      const int wk = idx >> 5, wc = idx & 31;
+      wr[i] = (k0 + wk < ke && n0 + wc < n) ? W[(int64_t)(k0 + wk) * g.ldw + n0 + wc] : 0.f;
+    }
+  };
+  float acc[4][4] = {};
+  if (kb < ke) load(kb);
+  for (int k0 = kb; k0 < ke; k0 += kC) {  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = lane + 64 * i;
+      Xs[w][idx & 15][idx >> 4] = xr[i];
+      Ws[w][idx >> 5][idx & 31] = wr[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (k0 + kC < ke) load(k0 + kC);
+#pragma unroll
+    for (int kk = 0; kk < kC; ++kk) {
+      float xa[4], wb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[i] = Xs[w][kk][4 * ty + i];
+        wb[i] = Ws[w][kk][4 * tx + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], wb[j], acc[i][j]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // reads done before the next chunk's writes
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[w][4 * ty + i][4 * tx + j] = acc[i][j];
+  __syncthreads();
+  // thread t sums the four partials of outputs 4 t .. 4 t + 3 (row t / 8, columns 4 (t % 8) ..)
+  const int r = tid >> 3, c0 = 4 * (tid & 7), row = m0 + r;
+  if (row < g.m) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + c0 + j;
+      if (col < n) {
+        float v = ((red[0][r][c0 + j] + red[1][r][c0 + j]) + red[2][r][c0 + j]) + red[3][r][c0 + j];
+        // optional epilogue: + bias[column], then max(0, .)
+        if (g.bias != nullptr) v += static_cast<const float*>(g.bias)[col];
+        if (args.relu) v = fmaxf(v, 0.f);
+        Y[(int64_t)row * g.ldy + col] = v;
+      }
+    }
+  }
+}
 }  // namespace
 
 hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream) {
@@ -78,6 +162,11 @@ hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream) {
   for (int i = 0; i < a.groups; ++i) max_m = a.g[i].m > max_m ? a.g[i].m : max_m;
   const int tiles_n = (a.n + kT - 1) / kT;
   const int tiles_m = (max_m + kT - 1) / kT;
+  if ((int64_t)tiles_n * tiles_m * a.groups < 256) {
+    const int sn = (a.n + 31) / 32, sm = (max_m + 31) / 32;
+    hipLaunchKernelGGL(linear_f32_splitk, dim3((unsigned)(sn * sm), (unsigned)a.groups), dim3(256), 0, stream, a, sn);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(tiles_n * tiles_m), (unsigned)a.groups);
   hipLaunchKernelGGL(linear_f32_kernel, grid, dim3(256), 0, stream, a, tiles_n);
   return hipGetLastError();
