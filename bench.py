@@ -214,6 +214,18 @@ def traffic_for(src_key, launch_desc):
     return rec.get("bytes_per_launch")
 
 
+def attention_kernel_name(n_q, causal, dtype):
+    """The forward kernel attention_forward runs for this shape: the bf16 form
+    with 64 query rows per wavefront or the one with 32 (the library's
+    attention_rows_per_wave rule), or the fp32 kernel."""
+    if dtype != "bf16":
+        return "attn_fwd_f32"
+    pad = (n_q + 255) // 256 * 256 - n_q
+    if (not causal and n_q >= 512 and pad == 0) or (n_q >= 2048 and pad * 16 <= n_q):
+        return "attn_fwd_bf16_d64_r64"
+    return "attn_fwd_bf16_d64_r32"
+
+
 def src_key_of(kernel):
     return ("linear" if kernel.startswith("linear") else "decode" if kernel.startswith("decode")
             else "backward" if kernel.startswith("attn_bwd") else "attention")
@@ -361,7 +373,7 @@ def mha_step_launches(mha, w, x, ws, kv_len, lens, dev):
     asets = [(rnd(B, N, H, d).transpose(1, 2), rnd(B, Nk, H, d).transpose(1, 2), rnd(B, Nk, H, d).transpose(1, 2),
               torch.empty((B, N, H, d), dtype=x.dtype, device=dev).transpose(1, 2)) for _ in range(n_a)]
     fa = lambda i: mha.attention_forward(*asets[i % n_a][:3], causal=w.causal, out=asets[i % n_a][3], kv_len=kv_len)
-    out.append({"launch": "attention", "kernel": "attn_fwd_bf16_d64" if w.dtype == "bf16" else "attn_fwd_f32",
+    out.append({"launch": "attention", "kernel": attention_kernel_name(N, w.causal, w.dtype),
                 "fn": fa, "flops": w.attention_flops(), "bytes": (2 * rq * dm + 2 * H * kv_rows * d) * esz,
                 "sets": n_a})
 
@@ -395,7 +407,7 @@ def time_secondary(mha, name, stream, dev, iters):
         sets = [(q, k, v)] + [(q.clone(), k.clone(), v.clone()) for _ in range(n_sets - 1)]
         outs = [torch.empty_like(q) for _ in range(n_sets)]
         fn = lambda i: mha.attention_forward(*sets[i % n_sets], causal=w.causal, out=outs[i % n_sets])
-        flops, peak, kernel = w.attention_flops(), PEAK_BF16_TFLOPS, "attn_fwd_bf16_d64"
+        flops, peak, kernel = w.attention_flops(), PEAK_BF16_TFLOPS, attention_kernel_name(w.n_q, w.causal, w.dtype)
     fn(0)
     torch.cuda.synchronize()
     ms = time_events(fn, iters, stream, lead_in=3, lead_seconds=LEAD_SECONDS)
@@ -568,7 +580,7 @@ def main():
         step(0)
         torch.cuda.synchronize()
         flops_step = w.attention_flops()
-        launches = [{"launch": "attention", "kernel": "attn_fwd_bf16_d64" if w.dtype == "bf16" else "attn_fwd_f32",
+        launches = [{"launch": "attention", "kernel": attention_kernel_name(w.n_q, w.causal, w.dtype),
                      "fn": step, "flops": flops_step, "bytes": per_set, "sets": n_sets}]
         get_out = lambda: outs[0]
 
