@@ -360,8 +360,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r32(AttnArgs a, floa
   for (int qb = 0; qb < kQB; ++qb) {
     const int my_q = q_wave0 + 32 * qb + lq;
     const bf16* src = qp + (int64_t)min(my_q, n_q - 1) * a.q_sn + 8 * hf;
+    // loads from a clamped (always valid) row, then rows past n_q are zeroed:
+    // a load under a per-lane condition would be waited for before the next
+    // one is issued, serialising the opening round trips
+    const unsigned keep = my_q < n_q ? 0xffffffffu : 0u;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = my_q < n_q ? (ld16(src + 16 * kk) ^ q_sign) : u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = (ld16(src + 16 * kk) ^ q_sign) & keep;
   }
 
   const int kv_end = kCausal ? min(n_k, qblk * kRows + kRows) : n_k;
@@ -652,14 +656,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r64(AttnArgs a, floa
   bf16* op = static_cast<bf16*>(a.o) + b_ * a.o_sb + h_ * a.o_sh;
   const int q_wave0 = qblk * kRows + wave * kRowsPerWave;
 
-  u32x4 qf[2][4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int my_q = q_wave0 + 32 * qb + lq;
-    const bf16* src = qp + (int64_t)min(my_q, n_q - 1) * a.q_sn + 8 * hf;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = my_q < n_q ? (ld16(src + 16 * kk) ^ q_sign) : u32x4{0, 0, 0, 0};
-  }
   const int kv_end = kCausal ? min(n_k, qblk * kRows + kRows) : n_k;
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
@@ -716,8 +712,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r64(AttnArgs a, floa
     st[qb].mc = 0.f;
     st[qb].l = 0.f;
   }
+  // Opening: tiles 0 and 1 and this wavefront's Q^T slices are fetched
+  // together, Q is complete before tile 2 is issued (so the wait for Q does
+  // not also wait for tiles 2 and 3).
   if (ntiles > 0) dma_tile(0);
   if (ntiles > 1) dma_tile(1);
+  // loads from a clamped (always valid) row, then rows past n_q are zeroed:
+  // a load under a per-lane condition would be waited for before the next
+  // one is issued, serialising the round trips
+  u32x4 qf[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_q = q_wave0 + 32 * qb + lq;
+    const bf16* src = qp + (int64_t)min(my_q, n_q - 1) * a.q_sn + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = ld16(src + 16 * kk);
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const unsigned keep = q_wave0 + 32 * qb + lq < n_q ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      qf[qb][kk] = (qf[qb][kk] ^ q_sign) & keep;
+      asm volatile("" : "+v"(qf[qb][kk]));  // complete here, before tile 2 is issued
+    }
+  }
   if (ntiles > 2) dma_tile(2);
 
   // fragments: set 0 for slab 0 of a tile, set 1 for slab 1
