@@ -216,14 +216,15 @@ def traffic_for(src_key, launch_desc):
 
 def attention_kernel_name(n_q, causal, dtype):
     """The forward kernel attention_forward runs for this shape: the bf16 form
-    with 64 query rows per wavefront or the one with 32 (the library's
-    attention_rows_per_wave rule), or the fp32 kernel."""
+    with 64 query rows per wavefront or one with 32 (the library's
+    attention_rows_per_wave rule; causal runs take the 32-row form with the
+    LDS load ring), or the fp32 kernel."""
     if dtype != "bf16":
         return "attn_fwd_f32"
     pad = (n_q + 255) // 256 * 256 - n_q
     if (not causal and n_q >= 512 and pad == 0) or (n_q >= 2048 and pad * 16 <= n_q):
         return "attn_fwd_bf16_d64_r64"
-    return "attn_fwd_bf16_d64_r32"
+    return "attn_fwd_bf16_d64_r32d" if causal else "attn_fwd_bf16_d64_r32"
 
 
 def src_key_of(kernel):

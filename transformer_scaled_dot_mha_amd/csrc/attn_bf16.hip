@@ -7,13 +7,16 @@
 // row maximum and row sum (the tiling idea the pages credit to FlashAttention,
 // "32 Transformer", "Connections"; re-derived here for CDNA4).
 //
-// Two kernel forms, both with workgroups of 4 wavefronts on one (batch, head)
+// Three kernel forms, all with workgroups of 4 wavefronts on one (batch, head)
 // and 64-key tiles staged through LDS:
-//   32 query rows per wavefront (128 per workgroup): short or ragged query
-//     runs. Tiles are double buffered: the next tile's global loads (raw
+//   32 query rows per wavefront (128 per workgroup): short or ragged unmasked
+//     query runs. Tiles are double buffered: the next tile's global loads (raw
 //     buffer loads; rows past the end read as zero) are in flight in
 //     registers while the current one is used, then written to LDS, V
 //     transposed ([d][key], two keys per 32-bit word).
+//   32 query rows per wavefront, causal: the same tile order on tiles loaded
+//     straight into a three-stage LDS ring (the 64-row form's layout), two
+//     tiles ahead.
 //   64 query rows per wavefront (two 32-row blocks sharing every K/V fragment
 //     read; 256 per workgroup): long query runs. Tiles go straight from global
 //     memory into a 4-stage LDS ring (buffer loads that write LDS) three tiles
@@ -819,6 +822,245 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r64(AttnArgs a, floa
   }
 }
 
+// ---------------------------------------------------------------------------
+// The 32-row form for causal runs: the same tile order as attend_tile (slab
+// 1's S^T MFMAs between slab 0's softmax quarters, slab 0's P V MFMAs between
+// slab 1's), with the tiles in the 64-row form's LDS layout, loaded straight
+// into a three-stage ring two tiles ahead (48 KB: three workgroups per CU).
+constexpr int kR32Stages = 3;
+
+template <bool kMasked, bool kFirst = false>
+__device__ __forceinline__ void attend_tile_f(RowState& st, const u32x4 (&qf)[4], const LdsFrags& fr, int last,
+                                              float c, const bf16x8& sel) {
+  u32x4 kf[2][4];
+#pragma unroll
+  for (int slab = 0; slab < 2; ++slab)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf[slab][kk] = fr.k(slab, kk);
+  auto rescore = [&](int slab) {
+    return [&, slab](float (&sv)[16]) {
+      f32x16 s = {};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) s = qk_one(s, fr.k(slab, kk), qf[kk]);
+      scores_of_impl<kMasked>(sv, s, slab, last);
+    };
+  };
+  u32x4 vf0[2][2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) vf0[jj][blk] = fr.v(0, jj, blk);
+  f32x16 s0 = {}, s1 = {};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) s0 = qk_one(s0, kf[0][kk], qf[kk]);
+  float sv0[16], sv1[16];
+  unsigned pw0[8], pw1[8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    s1 = qk_one(s1, kf[1][kk], qf[kk]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kk == 0) {
+      scores_of_impl<kMasked>(sv0, s0, 0, last);
+      if (kFirst) first_reference(st, sv0, c);
+    }
+    slab_weights<kMasked>(sv0, pw0, st.mc, c, 2 * kk, 2 * kk + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  check_reference<kMasked>(st, rescore(0), pw0, slab_rowsum(pw0, sel), c, sel);
+  u32x4 vf1[2][2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) vf1[jj][blk] = fr.v(1, jj, blk);
+  scores_of_impl<kMasked>(sv1, s1, 1, last);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pv_one(st, vf0[i >> 1][i & 1], pw0, i >> 1, i & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    slab_weights<kMasked>(sv1, pw1, st.mc, c, 2 * i, 2 * i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  check_reference<kMasked>(st, rescore(1), pw1, slab_rowsum(pw1, sel), c, sel);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pv_one(st, vf1[i >> 1][i & 1], pw1, i >> 1, i & 1);
+}
+
+template <bool kCausal>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r32d(AttnArgs a, float c, unsigned q_sign, int n_qblk) {
+  constexpr int kRowsPerWave = 32;
+  constexpr int kRows = 128;
+  __shared__ __attribute__((aligned(16))) char smem[kR32Stages * kStageBytes];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lq = lane & 31;
+  const int hf = lane >> 5;
+  const int n_q = a.n_q;
+  const bf16x8 sel = rowsum_selector(lane);
+
+  int bh, qblk;
+  if (kCausal) {
+    const int BH = a.batch * a.heads;
+    if ((BH & 7) == 0) {
+      const int x = blockIdx.x & 7, j = blockIdx.x >> 3, bhx = BH >> 3;
+      qblk = n_qblk - 1 - j / bhx;
+      bh = x + 8 * (j % bhx);
+    } else {
+      qblk = n_qblk - 1 - (int)(blockIdx.x / BH);
+      bh = (int)(blockIdx.x % BH);
+    }
+  } else {
+    const int total = gridDim.x, id = blockIdx.x;
+    const int per = total >> 3, rem = total & 7, x = id & 7, slot = id >> 3;
+    const int logical = (x < rem) ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
+    bh = logical / n_qblk;
+    qblk = logical - bh * n_qblk;
+  }
+  const int b_ = bh / a.heads, h_ = bh - b_ * a.heads;
+  const int n_k = a.kv_len != nullptr ? min(max(a.kv_len[b_], 0), a.n_k) : a.n_k;
+  const bf16* qp = static_cast<const bf16*>(a.q) + b_ * a.q_sb + h_ * a.q_sh;
+  const bf16* kp = static_cast<const bf16*>(a.k) + b_ * a.k_sb + h_ * a.k_sh;
+  const bf16* vp = static_cast<const bf16*>(a.v) + b_ * a.v_sb + h_ * a.v_sh;
+  bf16* op = static_cast<bf16*>(a.o) + b_ * a.o_sb + h_ * a.o_sh;
+  const int q_wave0 = qblk * kRows + wave * kRowsPerWave;
+  const int kv_end = kCausal ? min(n_k, qblk * kRows + kRows) : n_k;
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto dma_tile = [&](int tile) {
+    const int k0 = tile * kBN;
+    const int valid = min(n_k - k0, kBN);
+    const unsigned long long kb = (unsigned long long)(kp + (int64_t)k0 * a.k_sn);
+    const unsigned long long vb = (unsigned long long)(vp + (int64_t)k0 * a.v_sn);
+    auto uni = [](unsigned x) { return (unsigned)__builtin_amdgcn_readfirstlane((int)x); };
+    const u32x4 kr = {uni((unsigned)kb), uni((unsigned)(kb >> 32) & 0xffffu),
+                      uni(valid > 0 ? (unsigned)((valid - 1) * a.k_sn * 2 + 2 * 64) : 0u), (unsigned)kBufferFlags};
+    const u32x4 vr = {uni((unsigned)vb), uni((unsigned)(vb >> 32) & 0xffffu),
+                      uni(valid > 0 ? (unsigned)((valid - 1) * a.v_sn * 2 + 2 * 64) : 0u), (unsigned)kBufferFlags};
+    const unsigned st_base = uni(lds_off(smem) + (unsigned)((tile % kR32Stages) * kStageBytes));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int R = 16 * wave + 8 * i + (lane >> 3);
+      const int cch = (lane & 7) ^ (lane >> 3);
+      const int kr5 = R & 31;
+      const int key_k = (R & 32) | (kr5 & ~12) | ((kr5 >> 1) & 4) | ((kr5 << 1) & 8);
+      dma16(kr, (key_k * (int)a.k_sn + 8 * cch) * 2, st_base + (unsigned)((16 * wave_u + 8 * i) * kRowBytes));
+      dma16(vr, (R * (int)a.v_sn + 8 * cch) * 2, st_base + (unsigned)(64 * kRowBytes + (16 * wave_u + 8 * i) * kRowBytes));
+    }
+  };
+  LdsFrags fr0;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) fr0.klane[kk] = lq * kRowBytes + 16 * ((2 * kk + hf) ^ (lq & 7));
+  {
+    const int g = lane >> 4, j = lane & 15;
+    const int c_lane = 2 * (g & 1) + ((j & 3) >> 1);
+    fr0.vlane = (8 * (g >> 1) + (j >> 2)) * kRowBytes + 16 * (c_lane ^ (j >> 2)) + 8 * (j & 1);
+  }
+  fr0.base = smem;
+  auto frags_of = [&](int t) {
+    LdsFrags f = fr0;
+    f.base = smem + (t % kR32Stages) * kStageBytes;
+    return f;
+  };
+  // tile t has landed when at most the tiles issued after it are outstanding
+  // (4 loads per tile and wavefront); the barrier also ends every read of the
+  // stage that tile t + kR32Stages - 1 then reuses
+  auto tile_sync = [&](int t) {
+    const int ahead = min(kR32Stages - 2, ntiles - 1 - t);
+    if (kR32Stages >= 4 && ahead >= 2)
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (kR32Stages >= 3 && ahead == 1)
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + kR32Stages - 1 < ntiles) dma_tile(t + kR32Stages - 1);
+  };
+
+  // opening: tile 0 and Q together, the rest of the lead once Q is in
+  if (ntiles > 0) dma_tile(0);
+  u32x4 qf[4];
+  {
+    const int my_q = q_wave0 + lq;
+    const bf16* src = qp + (int64_t)min(my_q, n_q - 1) * a.q_sn + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = ld16(src + 16 * kk);
+    const unsigned keep = my_q < n_q ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      qf[kk] = (qf[kk] ^ q_sign) & keep;
+      asm volatile("" : "+v"(qf[kk]));
+    }
+  }
+  for (int t = 1; t < kR32Stages - 1 && t < ntiles; ++t) dma_tile(t);
+
+  RowState st;
+  st.o0 = f32x16{};
+  st.o1 = f32x16{};
+  st.m = -INFINITY;
+  st.mc = 0.f;
+  st.l = 0.f;
+
+  const int t_split = min(kCausal ? qblk * (kRows / kBN) : ntiles, n_k / kBN);
+  int t = 0;
+  if (t_split > 0) {
+    tile_sync(0);
+    attend_tile_f<false, true>(st, qf, frags_of(0), 0, c, sel);
+    t = 1;
+  }
+  for (; t < t_split; ++t) {
+    tile_sync(t);
+    attend_tile_f<false>(st, qf, frags_of(t), 0, c, sel);
+  }
+  for (; t < ntiles; ++t) {
+    tile_sync(t);
+    const int k0 = t * kBN;
+    if (!kCausal || k0 <= q_wave0 + kRowsPerWave - 1) {  // wave-uniform
+      const int last = (kCausal ? min(n_k - 1, q_wave0 + lq) : n_k - 1) - k0 - 8 * hf;
+      attend_tile_f<true>(st, qf, frags_of(t), last, c, sel);
+    }
+  }
+
+  {
+    const int my_q = q_wave0 + lq;
+    const float l_tot = st.l;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    unsigned w[2][4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      w[0][g][0] = pack_bf16(st.o0[4 * g] * inv, st.o0[4 * g + 1] * inv);
+      w[0][g][1] = pack_bf16(st.o0[4 * g + 2] * inv, st.o0[4 * g + 3] * inv);
+      w[1][g][0] = pack_bf16(st.o1[4 * g] * inv, st.o1[4 * g + 1] * inv);
+      w[1][g][1] = pack_bf16(st.o1[4 * g + 2] * inv, st.o1[4 * g + 3] * inv);
+    }
+    u32x4 chunk[2][2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        chunk[blk][tt] =
+            gather_row_chunk(w[blk][2 * tt][0], w[blk][2 * tt][1], w[blk][2 * tt + 1][0], w[blk][2 * tt + 1][1]);
+    if (my_q < n_q) {
+      bf16* dst = op + (int64_t)my_q * a.o_sn;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          *reinterpret_cast<u32x4*>(dst + 32 * blk + 8 * (2 * tt + hf)) = chunk[blk][tt];
+      if (a.lse != nullptr && hf == 0)
+        a.lse[(int64_t)bh * n_q + my_q] = l_tot > 0.f ? (st.mc + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+static void launch_r32d(const AttnArgs& a, hipStream_t stream, float c, unsigned q_sign) {
+  const int n_qblk = (a.n_q + 127) / 128;
+  const dim3 grid((unsigned)(n_qblk * a.batch * a.heads));
+  if (a.causal)
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r32d<true>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r32d<false>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+}
+
 static void launch_slab(const AttnArgs& a, hipStream_t stream, float c, unsigned q_sign) {
   const int n_qblk = (a.n_q + 255) / 256;
   const dim3 grid((unsigned)(n_qblk * a.batch * a.heads));
@@ -857,6 +1099,8 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
   const unsigned q_sign = a.scale < 0.f ? 0x80008000u : 0u;  // negate Q exactly: scale*s = |scale|*(-q).k
   if (attention_rows_per_wave(a.n_q, a.causal != 0) == 64)
     launch_slab(a, stream, c, q_sign);
+  else if (a.causal)
+    launch_r32d(a, stream, c, q_sign);
   else
     launch_rows32(a, stream, c, q_sign);
   return hipGetLastError();
