@@ -145,6 +145,26 @@ __device__ __forceinline__ void slab_weights(const float (&sv)[16], unsigned (&p
   }
 }
 
+// Weights of pairs [i0, i1) of slab `slab` from its raw (unmasked) scores;
+// on diagonal and ragged-end tiles the keys past `last` (relative to this
+// lane's first key of the tile) get weight 0 by their index, so the scores
+// themselves need no mask (a masked key's weight may be computed as inf or
+// NaN and is then replaced).
+template <bool kMasked>
+__device__ __forceinline__ void slab_weights_k(const float (&sv)[16], unsigned (&pw)[8], float mc, float c, int i0,
+                                               int i1, int slab, int last) {
+#pragma unroll
+  for (int i = i0; i < i1; ++i) {
+    float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c, -mc));
+    float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c, -mc));
+    if (kMasked) {
+      p0 = 32 * slab + 16 * ((2 * i) >> 3) + ((2 * i) & 7) <= last ? p0 : 0.f;
+      p1 = 32 * slab + 16 * ((2 * i + 1) >> 3) + ((2 * i + 1) & 7) <= last ? p1 : 0.f;
+    }
+    pw[i] = pack_bf16(p0, p1);
+  }
+}
+
 // Every weight is <= 2^8 while the reference holds. A weight above 2^8 (or
 // an overflow) makes the row's 32-weight slab sum exceed 2^8, so one compare per
 // slab detects when the reference must move; only then is the row maximum
@@ -216,7 +236,9 @@ __device__ __forceinline__ void mask_slab(float (&sv)[16], const f32x16& s, int 
 #pragma unroll
   for (int r = 0; r < 16; ++r) sv[r] = 32 * slab + 16 * (r >> 3) + (r & 7) <= last ? s[r] : -INFINITY;
 }
-// The slab's scores for the softmax: masked on diagonal and ragged-end tiles.
+// A slab's scores, masked (-inf past `last`) on diagonal and ragged-end tiles:
+// the rare reference move takes its row maximum from them. The common path
+// masks the weights instead (slab_weights_k).
 template <bool kMasked>
 __device__ __forceinline__ void scores_of_impl(float (&sv)[16], const f32x16& s, int slab, int last) {
   if (kMasked) {
@@ -242,7 +264,7 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
   // the slab's scores; on a wavefront's first (unmasked) tile, slab 0 also
   // sets its block's reference, so that its weights need no second pass
   auto scores_of = [&](float (&sv)[16], const f32x16& s, int slab, int lst, RowState& rs) {
-    scores_of_impl<kMasked>(sv, s, slab, lst);
+    scores_of_impl<false>(sv, s, slab, lst);  // masks are applied to the weights
     if (kFirst && slab == 0) first_reference(rs, sv, c);
   };
   u32x4 kf[2][4];
@@ -275,7 +297,7 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
       s1 = qk_one(s1, kf[1][kk], qf[0][kk]);
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 0) scores_of(sv0, s0, 0, last[0], st[0]);
-      slab_weights<kMasked>(sv0, pw0, st[0].mc, c, 2 * kk, 2 * kk + 2);
+      slab_weights_k<kMasked>(sv0, pw0, st[0].mc, c, 2 * kk, 2 * kk + 2, 0, last[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
     check_reference<kMasked>(st[0], rescore(0, 0), pw0, slab_rowsum(pw0, sel), c, sel);
@@ -289,7 +311,7 @@ __device__ __forceinline__ void attend_tile(RowState (&st)[kQB], const u32x4 (&q
     for (int i = 0; i < 4; ++i) {
       pv_one(st[0], vf0[i >> 1][i & 1], pw0, i >> 1, i & 1);
       __builtin_amdgcn_sched_barrier(0);
-      slab_weights<kMasked>(sv1, pw1, st[0].mc, c, 2 * i, 2 * i + 2);
+      slab_weights_k<kMasked>(sv1, pw1, st[0].mc, c, 2 * i, 2 * i + 2, 1, last[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
     check_reference<kMasked>(st[0], rescore(0, 1), pw1, slab_rowsum(pw1, sel), c, sel);
@@ -581,10 +603,10 @@ __device__ __forceinline__ void attend_slab(RowState (&st)[2], const u32x4 (&qf)
     sb = qk_one(sb, kf[kk], qf[B][kk]);
     __builtin_amdgcn_sched_barrier(0);
     if (kk == 0) {
-      scores_of_impl<kMasked>(sva, sa, slab, last[A]);
+      scores_of_impl<false>(sva, sa, slab, last[A]);  // masks are applied to the weights
       if (kFirst) first_reference(st[A], sva, c);
     }
-    slab_weights<kMasked>(sva, pwa, st[A].mc, c, 2 * kk, 2 * kk + 2);
+    slab_weights_k<kMasked>(sva, pwa, st[A].mc, c, 2 * kk, 2 * kk + 2, slab, last[A]);
     if (kk == 1) {  // the next slab's K fragments (this slab's are used by the MFMAs above)
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) kf_nxt[k2] = fn.k(nslab, k2);
@@ -592,9 +614,9 @@ __device__ __forceinline__ void attend_slab(RowState (&st)[2], const u32x4 (&qf)
     __builtin_amdgcn_sched_barrier(0);
   }
   const float psa = slab_rowsum(pwa, sel);
-  scores_of_impl<kMasked>(svb, sb, slab, last[B]);
+  scores_of_impl<false>(svb, sb, slab, last[B]);
   if (kFirst) first_reference(st[B], svb, c);
-  slab_weights<kMasked>(svb, pwb, st[B].mc, c, 0, 2);
+  slab_weights_k<kMasked>(svb, pwb, st[B].mc, c, 0, 2, slab, last[B]);
   __builtin_amdgcn_sched_barrier(0);
   check_reference<kMasked>(st[A], rescore(A), pwa, psa, c, sel);
   __builtin_amdgcn_sched_barrier(0);
@@ -602,7 +624,7 @@ __device__ __forceinline__ void attend_slab(RowState (&st)[2], const u32x4 (&qf)
   for (int j = 0; j < 4; ++j) {
     pv_one(st[A], vf[j >> 1][j & 1], pwa, j >> 1, j & 1);
     __builtin_amdgcn_sched_barrier(0);
-    if (j < 3) slab_weights<kMasked>(svb, pwb, st[B].mc, c, 2 * j + 2, 2 * j + 4);
+    if (j < 3) slab_weights_k<kMasked>(svb, pwb, st[B].mc, c, 2 * j + 2, 2 * j + 4, slab, last[B]);
     if (j == 1) {  // the next slab's V fragments go to the other register set
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
@@ -860,10 +882,10 @@ __device__ __forceinline__ void attend_tile_f(RowState& st, const u32x4 (&qf)[4]
     s1 = qk_one(s1, kf[1][kk], qf[kk]);
     __builtin_amdgcn_sched_barrier(0);
     if (kk == 0) {
-      scores_of_impl<kMasked>(sv0, s0, 0, last);
+      scores_of_impl<false>(sv0, s0, 0, last);  // masks are applied to the weights
       if (kFirst) first_reference(st, sv0, c);
     }
-    slab_weights<kMasked>(sv0, pw0, st.mc, c, 2 * kk, 2 * kk + 2);
+    slab_weights_k<kMasked>(sv0, pw0, st.mc, c, 2 * kk, 2 * kk + 2, 0, last);
     __builtin_amdgcn_sched_barrier(0);
   }
   check_reference<kMasked>(st, rescore(0), pw0, slab_rowsum(pw0, sel), c, sel);
@@ -872,12 +894,12 @@ __device__ __forceinline__ void attend_tile_f(RowState& st, const u32x4 (&qf)[4]
   for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) vf1[jj][blk] = fr.v(1, jj, blk);
-  scores_of_impl<kMasked>(sv1, s1, 1, last);
+  scores_of_impl<false>(sv1, s1, 1, last);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     pv_one(st, vf0[i >> 1][i & 1], pw0, i >> 1, i & 1);
     __builtin_amdgcn_sched_barrier(0);
-    slab_weights<kMasked>(sv1, pw1, st.mc, c, 2 * i, 2 * i + 2);
+    slab_weights_k<kMasked>(sv1, pw1, st.mc, c, 2 * i, 2 * i + 2, 1, last);
     __builtin_amdgcn_sched_barrier(0);
   }
   check_reference<kMasked>(st, rescore(1), pw1, slab_rowsum(pw1, sel), c, sel);
