@@ -222,7 +222,7 @@ def attention_kernel_name(n_q, causal, dtype):
     if dtype != "bf16":
         return "attn_fwd_f32"
     pad = (n_q + 255) // 256 * 256 - n_q
-    if (not causal and n_q >= 512 and pad == 0) or (n_q >= 2048 and pad * 16 <= n_q):
+    if (not causal and n_q >= 512 and pad == 0) or (n_q >= (4096 if causal else 2048) and pad * 16 <= n_q):
         return "attn_fwd_bf16_d64_r64"
     return "attn_fwd_bf16_d64_r32d" if causal else "attn_fwd_bf16_d64_r32"
 

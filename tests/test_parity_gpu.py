@@ -114,13 +114,16 @@ EDGE = [
     (1, 2, 5, 300, False, "bf16"),
     (1, 1, 257, 1, False, "bf16"),
     (2, 1, 1500, 1650, False, "bf16"),
-    # 64 query rows per wavefront (two 32-row blocks, long query runs): ragged tails
+    # 64 query rows per wavefront (two 32-row blocks, long query runs: causal from 4096 queries,
+    # unmasked from 2048) on both sides of the rule, with ragged tails
     (2, 2, 2048, 2048, True, "bf16"),
     (1, 1, 2049, 2049, True, "bf16"),
     (1, 3, 2600, 2600, True, "bf16"),
     (1, 2, 3000, 3000, True, "bf16"),
-    (1, 1, 2500, 2600, False, "bf16"),
+    (1, 1, 4095, 4095, True, "bf16"),
+    (1, 1, 4096, 4096, True, "bf16"),
     (1, 1, 4100, 4100, True, "bf16"),
+    (1, 1, 2500, 2600, False, "bf16"),
     # unmasked query runs that fill whole 256-row workgroups also take 64 rows per wavefront;
     # ragged key counts on either side of a key tile, and 640 rows (which stays at 32)
     (2, 2, 512, 300, False, "bf16"),
@@ -380,7 +383,9 @@ PADDED = [
     # 64 query rows per wavefront (whole 256-row workgroups) under per-item lengths:
     # 0, below one slab, not a multiple of 64, full
     (4, 2, 512, 512, False, "bf16", [512, 300, 37, 0]),
-    (1, 2, 2048, 2048, True, "bf16", [1000]),
+    (1, 2, 4096, 4096, True, "bf16", [1000]),
+    (2, 1, 4096, 4096, True, "bf16", [4096, 2100]),
+    # the causal 32-row form under the same kind of lengths
     (2, 2, 2048, 2048, True, "bf16", [2048, 1000]),
     (3, 1, 768, 1000, False, "bf16", [1000, 63, 513]),
     (3, 2, 70, 90, False, "f32", [90, 33, 0]),
