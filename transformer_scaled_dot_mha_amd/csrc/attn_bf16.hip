@@ -177,7 +177,8 @@ __device__ __forceinline__ void slab_weights_k(const float (&sv)[16], unsigned (
 template <bool kMasked, typename Rescore>
 __device__ __forceinline__ void check_reference(RowState& st, Rescore&& rescore, unsigned (&pw)[8], float ps, float c,
                                                 const bf16x8& sel) {
-  const bool bad = !(ps <= kMaxSlabSum) || st.m == -INFINITY;
+  // an unmasked tile comes after the block's first (unmasked) slab has set the reference
+  const bool bad = !(ps <= kMaxSlabSum) || (kMasked && st.m == -INFINITY);
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) {
     asm volatile("" ::: "memory");  // keep a real branch, not predicated code
     // the slab's scores again (their registers are not kept for this rare path)
