@@ -385,8 +385,9 @@ PADDED = [
     (4, 2, 512, 512, False, "bf16", [512, 300, 37, 0]),
     (1, 2, 4096, 4096, True, "bf16", [1000]),
     (2, 1, 4096, 4096, True, "bf16", [4096, 2100]),
-    # the causal 32-row form under the same kind of lengths
+    # the causal 32-row form under the same kind of lengths, 0 and below one slab included
     (2, 2, 2048, 2048, True, "bf16", [2048, 1000]),
+    (3, 2, 300, 300, True, "bf16", [0, 5, 300]),
     (3, 1, 768, 1000, False, "bf16", [1000, 63, 513]),
     (3, 2, 70, 90, False, "f32", [90, 33, 0]),
     (2, 2, 65, 65, True, "f32", [65, 7]),
@@ -412,18 +413,19 @@ def test_padded_attention_parity(dev, B, H, nq, nk, causal, dtype, lens):
     assert max_abs(got_lse[~dead], want_lse[~dead]) <= LSE_TOL[dtype], "log-sum-exp under padding"
 
 
-def test_padded_keys_are_never_read(dev):
+@pytest.mark.parametrize("causal", [False, True])
+def test_padded_keys_are_never_read(dev, causal):
     """Changing K and V past a batch item's length leaves the output bitwise unchanged."""
     import torch
     B, H, n = 2, 2, 300
     q, k, v = (to_device(workloads.random_tensor((B, H, n, 64), "bf16", seed=800 + i), dev) for i in range(3))
     kv_len = torch.tensor([300, 111], dtype=torch.int32, device=dev)
-    say("padded keys never read")
-    a = mha.attention_forward(q, k, v, kv_len=kv_len)
+    say(f"padded keys never read, causal={causal}")
+    a = mha.attention_forward(q, k, v, causal=causal, kv_len=kv_len)
     k2, v2 = k.clone(), v.clone()
     k2[1, :, 111:] = 30.0
     v2[1, :, 111:] = float("nan")
-    b = mha.attention_forward(q, k2, v2, kv_len=kv_len)
+    b = mha.attention_forward(q, k2, v2, causal=causal, kv_len=kv_len)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
