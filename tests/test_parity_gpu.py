@@ -267,18 +267,24 @@ def test_key_permutation_invariance_on_gpu(dev):
 # ---------------------------------------------------------------- projections and full MHA variants
 def _linear_tile_rows(m, n, groups=1):
     """Tile height the bf16 projection launcher picks (its rule restated here
-    so that each case below is known to reach the form it is meant for): the
-    height whose workgroup count fills whole rounds of 512 best, 128 on ties."""
+    so that each case below is known to reach the form it is meant for): 64
+    rows when the 128-row grid has fewer workgroups than CUs, else the height
+    whose workgroup count fills whole rounds of 512 best, 128 on ties."""
     tiles_n = (n + 127) // 128
     big = tiles_n * ((m + 255) // 256) * groups
     small = tiles_n * ((m + 127) // 128) * groups
+    if small < 256:
+        return 64
     fill = lambda w: w / (((w + 511) // 512) * 512)
     return 256 if big >= 512 and fill(big) > fill(small) else 128
 
 
 LINEAR_CASES = [
+    # 64-row tiles (grids smaller than the CU count), ragged m, n and k
     (1, 8, 8, "bf16"), (300, 136, 72, "bf16"), (2048, 512, 512, "bf16"), (257, 520, 136, "bf16"),
-    (1000, 1536, 512, "bf16"), (64, 128, 1040, "bf16"), (16384, 512, 512, "bf16"),
+    (1000, 1536, 512, "bf16"), (64, 128, 1040, "bf16"),
+    # 128-row tiles
+    (16384, 512, 512, "bf16"), (4100, 1096, 200, "bf16"),
     # 256-row tiles: 512 workgroups fill whole rounds, with ragged m and a partial last k chunk
     (8000, 2048, 520, "bf16"), (32513, 512, 512, "bf16"), (32640, 512, 512, "bf16"),
     # fp32: split-k form (small grids; k quarters of 16, 48 and 64 with a ragged last one), and the 64 x 64 form
@@ -304,7 +310,7 @@ def test_linear_parity(dev, m, n, k, dtype):
 def test_linear_cases_reach_both_tile_heights():
     """The case list above selects both bf16 tile forms and both fp32 forms (a host-side check of the list)."""
     heights = {_linear_tile_rows(m, n) for m, n, k, dt in LINEAR_CASES if dt == "bf16"}
-    assert heights == {128, 256}
+    assert heights == {64, 128, 256}
     assert {_linear_f32_form(m, n) for m, n, k, dt in LINEAR_CASES if dt == "f32"} == {"split-k", "64x64"}
 
 
