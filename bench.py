@@ -214,6 +214,15 @@ def traffic_for(src_key, launch_desc):
     return rec.get("bytes_per_launch")
 
 
+def linear_kernel_name(m, n, groups, dtype):
+    """The projection kernel linear_forward(_grouped) runs for this shape: the
+    bf16 tile kernel (every tile height), or the fp32 split-k form for grids
+    of fewer than 256 64 x 64 tiles, else the fp32 tile kernel."""
+    if dtype == "bf16":
+        return "linear_bf16_kernel"
+    return "linear_f32_splitk" if ((n + 63) // 64) * ((m + 63) // 64) * groups < 256 else "linear_f32_kernel"
+
+
 def attention_kernel_name(n_q, causal, dtype):
     """The forward kernel attention_forward runs for this shape: the bf16 form
     with 64 query rows per wavefront or one with 32 (the library's
@@ -363,7 +372,7 @@ def mha_step_launches(mha, w, x, ws, kv_len, lens, dev):
     qsets = [(x.view(rq, dm) if i == 0 else rnd(rq, dm),
               [torch.empty((r, dm), dtype=x.dtype, device=dev) for r in (rq, rk, rk)]) for i in range(n_q)]
     fq = lambda i: mha.linear_forward_grouped([qsets[i % n_q][0]] * 3, ws[:3], outs=qsets[i % n_q][1])
-    out.append({"launch": "qkv_projection", "kernel": "linear_bf16_kernel", "fn": fq,
+    out.append({"launch": "qkv_projection", "kernel": linear_kernel_name(max(rq, rk), dm, 3, w.dtype), "fn": fq,
                 "flops": 2 * dm * dm * (rq + 2 * rk), "bytes": (rq * dm + 3 * dm * dm + (rq + 2 * rk) * dm) * esz,
                 "sets": n_q})
 
@@ -383,7 +392,7 @@ def mha_step_launches(mha, w, x, ws, kv_len, lens, dev):
     n_o = max(1, math.ceil(ROTATE_BYTES / per))
     osets = [(rnd(rq, dm), torch.empty((rq, dm), dtype=x.dtype, device=dev)) for _ in range(n_o)]
     fo = lambda i: mha.linear_forward(osets[i % n_o][0], ws[3], out=osets[i % n_o][1])
-    out.append({"launch": "output_projection", "kernel": "linear_bf16_kernel", "fn": fo,
+    out.append({"launch": "output_projection", "kernel": linear_kernel_name(rq, dm, 1, w.dtype), "fn": fo,
                 "flops": 2 * rq * dm * dm, "bytes": (2 * rq * dm + dm * dm) * esz, "sets": n_o})
     return out
 

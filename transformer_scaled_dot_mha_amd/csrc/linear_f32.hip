@@ -8,10 +8,11 @@
 // a bias per column and a ReLU (the FFN's max(0, x W1 + b1)).
 //
 // Grids of fewer than 256 such tiles (a single short sequence) take a second
-// form instead: 32 x 32 tiles whose four wavefronts each run a quarter of k
-// (their own LDS chunks, the next chunk's loads in flight in registers), the
-// four partial tiles summed at the end, so that short problems spread over
-// many wavefronts instead of long serial k loops.
+// form instead: 32 x 32 tiles whose sixteen wavefronts (one 1024-thread
+// workgroup) each run a sixteenth of k (their own LDS chunks, the next
+// chunk's loads in flight in registers), the partial tiles summed at the end
+// in wavefront order, so that short problems spread over many wavefronts
+// instead of long serial k loops.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -81,11 +82,13 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(LinearArgs args, int ti
 // 32 x 32 output tile; wavefront w runs k range [w kq, (w + 1) kq) in
 // 16-deep chunks staged in its own LDS region; lane (ty, tx) = (lane / 8,
 // lane % 8) accumulates rows 4 ty.., columns 4 tx..
-__global__ __launch_bounds__(256) void linear_f32_splitk(LinearArgs args, int tiles_n) {
+constexpr int kSW = 16;  // wavefronts per split-k workgroup, one k range each
+
+__global__ __launch_bounds__(64 * kSW) void linear_f32_splitk(LinearArgs args, int tiles_n) {
   constexpr int kS = 32, kC = 16;
-  __shared__ float Xs[4][kC][kS + 4];
-  __shared__ float Ws[4][kC][kS];
-  __shared__ float red[4][kS][kS + 1];
+  __shared__ float Xs[kSW][kC][kS + 4];
+  __shared__ float Ws[kSW][kC][kS];
+  __shared__ float red[kSW][kS][kS + 1];
   const LinearGroup g = blockIdx.y == 0 ? args.g[0] : (blockIdx.y == 1 ? args.g[1] : args.g[2]);
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
   const int m0 = tm * kS, n0 = tn * kS;
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void linear_f32_splitk(LinearArgs args, int ti
   const float* W = static_cast<const float*>(g.w);
   float* Y = static_cast<float*>(g.y);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, tx = lane & 7, ty = lane >> 3;
-  const int kq = (kdim + 4 * kC - 1) / (4 * kC) * kC;  // each wavefront's k range, a multiple of 16
+  const int kq = (kdim + kSW * kC - 1) / (kSW * kC) * kC;  // each wavefront's k range, a multiple of 16
   const int kb = w * kq, ke = min(kdim, kb + kq);
   float xr[8], wr[8];
   auto load = [&](int k0) {
@@ -139,20 +142,16 @@ __global__ __launch_bounds__(256) void linear_f32_splitk(LinearArgs args, int ti
 #pragma unroll
     for (int j = 0; j < 4; ++j) red[w][4 * ty + i][4 * tx + j] = acc[i][j];
   __syncthreads();
-  // thread t sums the four partials of outputs 4 t .. 4 t + 3 (row t / 8, columns 4 (t % 8) ..)
-  const int r = tid >> 3, c0 = 4 * (tid & 7), row = m0 + r;
-  if (row < g.m) {
+  // thread t sums the kSW partials of output t (row t / 32, column t % 32), in wavefront order
+  const int r = tid >> 5, cc = tid & 31, row = m0 + r, col = n0 + cc;
+  if (row < g.m && col < n) {
+    float v = red[0][r][cc];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + c0 + j;
-      if (col < n) {
-        float v = ((red[0][r][c0 + j] + red[1][r][c0 + j]) + red[2][r][c0 + j]) + red[3][r][c0 + j];
-        // optional epilogue: + bias[column], then max(0, .)
-        if (g.bias != nullptr) v += static_cast<const float*>(g.bias)[col];
-        if (args.relu) v = fmaxf(v, 0.f);
-        Y[(int64_t)row * g.ldy + col] = v;
-      }
-    }
+    for (int q = 1; q < kSW; ++q) v += red[q][r][cc];
+    // optional epilogue: + bias[column], then max(0, .)
+    if (g.bias != nullptr) v += static_cast<const float*>(g.bias)[col];
+    if (args.relu) v = fmaxf(v, 0.f);
+    Y[(int64_t)row * g.ldy + col] = v;
   }
 }
 }  // namespace
@@ -164,7 +163,7 @@ hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream) {
   const int tiles_m = (max_m + kT - 1) / kT;
   if ((int64_t)tiles_n * tiles_m * a.groups < 256) {
     const int sn = (a.n + 31) / 32, sm = (max_m + 31) / 32;
-    hipLaunchKernelGGL(linear_f32_splitk, dim3((unsigned)(sn * sm), (unsigned)a.groups), dim3(256), 0, stream, a, sn);
+    hipLaunchKernelGGL(linear_f32_splitk, dim3((unsigned)(sn * sm), (unsigned)a.groups), dim3(64 * kSW), 0, stream, a, sn);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(tiles_n * tiles_m), (unsigned)a.groups);
