@@ -53,15 +53,23 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(AttnArgs a, float c, float q
   const int q0 = qb * kRows;
   const int my_q = q0 + r;
 
+  // Loads go to clamped (always valid) rows and out-of-range values are
+  // zeroed afterwards: a load under a per-lane condition would be waited for
+  // before the next one is issued.
   float q[kPart], acc[kPart];
+  {
+    const float* src = qp + (int64_t)min(my_q, n_q - 1) * a.q_sn + part * kPart;
+    float4 v[kPart / 4];
 #pragma unroll
-  for (int t = 0; t < kPart; t += 4) {
-    const float4 v = my_q < n_q ? *reinterpret_cast<const float4*>(qp + (int64_t)my_q * a.q_sn + part * kPart + t)
-                                : float4{0.f, 0.f, 0.f, 0.f};
-    q[t] = q_sign * v.x;
-    q[t + 1] = q_sign * v.y;
-    q[t + 2] = q_sign * v.z;
-    q[t + 3] = q_sign * v.w;
+    for (int t = 0; t < kPart; t += 4) v[t / 4] = *reinterpret_cast<const float4*>(src + t);
+    const bool row_ok = my_q < n_q;
+#pragma unroll
+    for (int t = 0; t < kPart; t += 4) {
+      q[t] = row_ok ? q_sign * v[t / 4].x : 0.f;
+      q[t + 1] = row_ok ? q_sign * v[t / 4].y : 0.f;
+      q[t + 2] = row_ok ? q_sign * v[t / 4].z : 0.f;
+      q[t + 3] = row_ok ? q_sign * v[t / 4].w : 0.f;
+    }
   }
 #pragma unroll
   for (int t = 0; t < kPart; ++t) acc[t] = 0.f;
@@ -71,19 +79,34 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(AttnArgs a, float c, float q
   float* Ks = smem + wave * 2 * kTile;
   float* Vs = Ks + kTile;
 
+#pragma unroll 1
   for (int ti = wave; ti < ntile; ti += 4) {  // wave-uniform
     const int k0 = ti * kKeys;
     // this wavefront's tile (only its own lanes read it, so no barrier)
+    constexpr int kLoads = kTile / 4 / 64;  // float4 loads of K (and of V) per lane
+    constexpr int kGroup = kLoads < 4 ? kLoads : 4;
 #pragma unroll
-    for (int i = lane; i < kTile / 4; i += 64) {
-      const int key = i / (D / 4), c4 = 4 * (i - key * (D / 4));
-      const bool in = k0 + key < n_k;
-      const float4 kv = in ? *reinterpret_cast<const float4*>(kp + (int64_t)(k0 + key) * a.k_sn + c4)
-                           : float4{0.f, 0.f, 0.f, 0.f};
-      const float4 vv = in ? *reinterpret_cast<const float4*>(vp + (int64_t)(k0 + key) * a.v_sn + c4)
-                           : float4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<float4*>(Ks + key * D + c4) = kv;
-      *reinterpret_cast<float4*>(Vs + key * D + c4) = vv;
+    for (int u0 = 0; u0 < kLoads; u0 += kGroup) {  // groups of loads in flight together
+      float4 kv[kGroup], vv[kGroup];
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        const int i = lane + 64 * (u0 + u);
+        const int key = i / (D / 4), c4 = 4 * (i - key * (D / 4));
+        const int row = min(k0 + key, n_k - 1);  // n_k >= 1 here: the tile holds a visible key
+        kv[u] = *reinterpret_cast<const float4*>(kp + (int64_t)row * a.k_sn + c4);
+        vv[u] = *reinterpret_cast<const float4*>(vp + (int64_t)row * a.v_sn + c4);
+      }
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        const int i = lane + 64 * (u0 + u);
+        const int key = i / (D / 4), c4 = 4 * (i - key * (D / 4));
+        const bool in = k0 + key < n_k;
+        // component selects (a select of whole float4 structs goes through scratch memory)
+        const float4 kz = {in ? kv[u].x : 0.f, in ? kv[u].y : 0.f, in ? kv[u].z : 0.f, in ? kv[u].w : 0.f};
+        const float4 vz = {in ? vv[u].x : 0.f, in ? vv[u].y : 0.f, in ? vv[u].z : 0.f, in ? vv[u].w : 0.f};
+        *reinterpret_cast<float4*>(Ks + key * D + c4) = kz;
+        *reinterpret_cast<float4*>(Vs + key * D + c4) = vz;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     float s[kKeys];
