@@ -222,6 +222,28 @@ def test_reference_moves_in_long_query_runs(dev, scale, causal):
     assert max_abs(to_f64(lse), want_lse) <= LSE_TOL["bf16"], "log-sum-exp"
 
 
+@pytest.mark.parametrize("n,causal", [(300, False), (512, False), (2048, True), (4096, True)])
+def test_weights_beyond_the_float_range(dev, n, causal):
+    """At scale 12 the scores of one row span several hundred binary orders: a
+    row's maximum exceeds the maximum of its first 32 keys by up to ~500 of them
+    (274 of the 512 rows, 2947 of the 4096 rows by 128 or more, so weights against
+    that first reference would overflow fp32). The running reference must move
+    on unmasked tiles without any weight against an outdated reference reaching
+    O or the row sum as inf. 512 and 4096 rows take the 64-row kernel form, 300
+    and 2048 the 32-row forms (unmasked, and causal with the three-stage ring)."""
+    import torch
+    q = workloads.random_tensor((1, 1, n, 64), "bf16", seed=71)
+    k = workloads.random_tensor((1, 1, n, 64), "bf16", seed=72)
+    v = workloads.random_tensor((1, 1, n, 64), "bf16", seed=73)
+    say(f"overflowing weights n={n} causal={causal}")
+    o, lse = mha.attention_forward(to_device(q, dev), to_device(k, dev), to_device(v, dev), causal=causal,
+                                   scale=12.0, return_lse=True)
+    torch.cuda.synchronize()
+    want, _, want_lse = oracle.attention_ref(q.value, k.value, v.value, causal=causal, scale=12.0)
+    assert_close(to_f64(o), want, "bf16", f"scale 12 causal {causal}")
+    assert max_abs(to_f64(lse), want_lse) <= LSE_TOL["bf16"], "log-sum-exp"
+
+
 # ---------------------------------------------------------------- properties on GPU outputs
 def test_deterministic(dev):
     import torch
