@@ -46,7 +46,8 @@
 // tile whose first key lies past the wavefront's last query is skipped; only
 // tiles that straddle the diagonal (or the ragged end) apply per-element masks.
 // Causal workgroups run heaviest query block first, with each head's blocks
-// on one XCD.
+// on one XCD (the 32-row causal form puts the lightest levels first when its
+// grid overflows one round of resident workgroups by at most a round).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -909,7 +910,7 @@ __device__ __forceinline__ void attend_tile_f(RowState& st, const u32x4 (&qf)[4]
 }
 
 template <bool kCausal>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r32d(AttnArgs a, float c, unsigned q_sign, int n_qblk) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r32d(AttnArgs a, float c, unsigned q_sign, int n_qblk, int n_light) {
   constexpr int kRowsPerWave = 32;
   constexpr int kRows = 128;
   __shared__ __attribute__((aligned(16))) char smem[kR32Stages * kStageBytes];
@@ -923,15 +924,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r32d(AttnArgs a, flo
 
   int bh, qblk;
   if (kCausal) {
+    // dispatch level r of the query blocks: the n_light lightest levels
+    // first (they would otherwise start in a late, partial second round of
+    // workgroups, each with its own opening), then the others heaviest first
     const int BH = a.batch * a.heads;
+    int r;
     if ((BH & 7) == 0) {
       const int x = blockIdx.x & 7, j = blockIdx.x >> 3, bhx = BH >> 3;
-      qblk = n_qblk - 1 - j / bhx;
+      r = j / bhx;
       bh = x + 8 * (j % bhx);
     } else {
-      qblk = n_qblk - 1 - (int)(blockIdx.x / BH);
+      r = (int)(blockIdx.x / BH);
       bh = (int)(blockIdx.x % BH);
     }
+    qblk = r < n_light ? n_light - 1 - r : n_qblk - 1 - (r - n_light);
   } else {
     const int total = gridDim.x, id = blockIdx.x;
     const int per = total >> 3, rem = total & 7, x = id & 7, slot = id >> 3;
@@ -1075,13 +1081,38 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r32d(AttnArgs a, flo
   }
 }
 
+// Workgroups of the causal 32-row form the current device holds at once
+// (occupancy x compute units), cached per device; 0 if the query fails.
+static int r32d_resident() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] != 0) return cache[dev] > 0 ? cache[dev] : 0;
+  int occ = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_fwd_bf16_d64_r32d<true>, 256, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || occ * cus <= 0) {
+    cache[dev] = -1;
+    return 0;
+  }
+  cache[dev] = occ * cus;
+  return cache[dev];
+}
+
 static void launch_r32d(const AttnArgs& a, hipStream_t stream, float c, unsigned q_sign) {
   const int n_qblk = (a.n_q + 127) / 128;
-  const dim3 grid((unsigned)(n_qblk * a.batch * a.heads));
+  const int BH = a.batch * a.heads;
+  const int n_items = n_qblk * BH;
+  // causal grids that overflow one round of resident workgroups by at most a
+  // round: as many of the lightest levels as overflow go first
+  int n_light = 0;
+  const int resident = a.causal ? r32d_resident() : 0;
+  if (resident > 0 && n_items > resident && n_items <= 2 * resident)
+    n_light = min((n_items - resident + BH - 1) / BH, n_qblk);
+  const dim3 grid((unsigned)n_items);
   if (a.causal)
-    hipLaunchKernelGGL((attn_fwd_bf16_d64_r32d<true>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r32d<true>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk, n_light);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_d64_r32d<false>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r32d<false>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk, 0);
 }
 
 static void launch_slab(const AttnArgs& a, hipStream_t stream, float c, unsigned q_sign) {
