@@ -416,6 +416,8 @@ PADDED = [
     # the causal 32-row form under the same kind of lengths, 0 and below one slab included
     (2, 2, 2048, 2048, True, "bf16", [2048, 1000]),
     (3, 2, 300, 300, True, "bf16", [0, 5, 300]),
+    # 800 causal 32-row workgroups overflow one round of 768 resident ones: the lightest level goes first
+    (50, 8, 256, 256, True, "bf16", [256, 0, 37, 1, 200, 129, 64, 255] * 6 + [256, 100]),
     (3, 1, 768, 1000, False, "bf16", [1000, 63, 513]),
     (3, 2, 70, 90, False, "f32", [90, 33, 0]),
     (2, 2, 65, 65, True, "f32", [65, 7]),
