@@ -52,7 +52,8 @@ LEAD_SECONDS = 0.2          # back-to-back launches ahead of each timed pass
 SCLK_PLAUSIBLE_MHZ = (500, 2400)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "attention": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_bf16.hip"),
+    "attention": [os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_bf16.hip"),
+                  os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_fwd_loop.inc")],
     "linear": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "linear_bf16.hip"),
     "decode": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "decode.hip"),
     "backward": os.path.join(ROOT, "transformer_scaled_dot_mha_amd", "csrc", "attn_bwd_bf16.hip"),
@@ -64,10 +65,12 @@ def log(msg):
 
 
 def source_sha(path):
-    """Hash of a kernel source's code: comments and blank lines do not count,
-    so a comment edit keeps the recorded counters valid."""
-    with open(path) as f:
-        text = f.read()
+    """Hash of a kernel source's code (one file or a list of them): comments and
+    blank lines do not count, so a comment edit keeps the recorded counters valid."""
+    text = ""
+    for p in ([path] if isinstance(path, str) else path):
+        with open(p) as f:
+            text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
     code = "\n".join(ln for ln in lines if ln.strip())

@@ -64,6 +64,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBN = 64;        // keys per tile
 constexpr int kPitch = 72;     // LDS row pitch, bf16 elements (144 bytes: conflict-free 16-byte reads)
@@ -539,6 +540,9 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 constexpr int kRowBytes = 128;
 constexpr int kStageBytes = 2 * 64 * kRowBytes;
 constexpr int kNStages = 4;
+
+// fwd_loop_asm: the steady-state unmasked tile loop of the 64-row form
+#include "attn_fwd_loop.inc"
 struct LdsFrags {
   const char* base;  // generic pointer to the stage
   int klane[4];      // per-lane byte offsets of K fragments kk = 0..3 (slab 0)
@@ -652,7 +656,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r64(AttnArgs a, floa
   const int lq = lane & 31;
   const int hf = lane >> 5;
   const int n_q = a.n_q;
-  const bf16x8 sel = rowsum_selector(lane);
+  bf16x8 sel = rowsum_selector(lane);
 
   int bh, qblk;
   if (kCausal) {
@@ -803,9 +807,51 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r64(AttnArgs a, floa
     if (1 < ntiles) tile_sync(1);
     t = 1;
   }
-  for (; t < t_split; ++t) {
-    tile(F{}, F{}, t);
-    if (t + 1 < ntiles) tile_sync(t + 1);
+  if (t_split > 1) {
+    // Unmasked tiles 1 .. t_split-1: the hand-scheduled loop (same arithmetic,
+    // fixed issue order). On entry tiles 1 and 2 are in LDS and tiles 3 and 4
+    // are requested; it requests tiles 5 .. t_split+2 itself (three ahead, as
+    // tile_sync does) and leaves every wavefront past its last LDS read.
+    const unsigned smem_lds = lds_off(smem);
+    u32x4 kl;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kl[kk] = smem_lds + (unsigned)fr0.klane[kk];
+    const unsigned vl = smem_lds + 64 * kRowBytes + (unsigned)fr0.vlane;
+    unsigned dk[2], dv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int R = 16 * wave + 8 * i + (lane >> 3);
+      const int cch = (lane & 7) ^ (lane >> 3);
+      const int kr5 = R & 31;
+      const int key_k = (R & 32) | (kr5 & ~12) | ((kr5 >> 1) & 4) | ((kr5 << 1) & 8);
+      dk[i] = (unsigned)((key_k * (int)a.k_sn + 8 * cch) * 2);
+      dv[i] = (unsigned)((R * (int)a.v_sn + 8 * cch) * 2);
+    }
+    auto uni = [](unsigned x) { return (unsigned)__builtin_amdgcn_readfirstlane((int)x); };
+    const unsigned long long kb5 = (unsigned long long)kp + (unsigned long long)(5 * kBN) * a.k_sn * 2;
+    const unsigned long long vb5 = (unsigned long long)vp + (unsigned long long)(5 * kBN) * a.v_sn * 2;
+    u32x4 sel_u = __builtin_bit_cast(u32x4, sel);
+    fwd_loop_asm(st[0].o0, st[0].o1, st[1].o0, st[1].o1, st[0].m, st[1].m, st[0].mc, st[1].mc, st[0].l, st[1].l,
+                 qf, sel_u, kl, vl, dk[0], dk[1], dv[0], dv[1], c, t_split - 1, ntiles,
+                 n_k - 5 * kBN, (int)uni((unsigned)(a.k_sn * 2)), (int)uni((unsigned)(a.v_sn * 2)),
+                 uni((unsigned)(kBN * a.k_sn * 2)), uni((unsigned)(kBN * a.v_sn * 2)),
+                 uni(smem_lds + (unsigned)(16 * wave_u * kRowBytes)), uni((unsigned)kb5), uni((unsigned)(kb5 >> 32)),
+                 uni((unsigned)vb5), uni((unsigned)(vb5 >> 32)));
+    // the selector comes back from the loop unchanged; using its copy keeps
+    // the compiler from holding a second one across it
+    sel = __builtin_bit_cast(bf16x8, sel_u);
+    t = t_split;
+    if (t < ntiles) tile_sync(t);
+    // the next tile's slab-0 fragments (when no tile follows, these in-bounds
+    // reads are not used; reading them unconditionally keeps the fragments
+    // from before the loop dead across it)
+    const LdsFrags f = frags_of(t);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf0[kk] = f.k(0, kk);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) vf0[jj][blk] = f.v(0, jj, blk);
   }
   for (; t < ntiles; ++t) {
     const int k0 = t * kBN;
