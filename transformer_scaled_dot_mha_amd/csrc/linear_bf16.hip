@@ -103,8 +103,11 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
   constexpr int kStageBytes = kXBytes + kTK * kWRow;
   constexpr int kXDma = kTM / 64;  // X loads per wavefront per chunk (16 rows of 64 B each)
   constexpr int kWDma = 2;         // W loads per wavefront per chunk (4 rows of 256 B each)
-  // the stages, and afterwards the output tile (kTM rows of 256 bytes)
-  constexpr int kSmem = kNStages * kStageBytes > kTM * kWRow ? kNStages * kStageBytes : kTM * kWRow;
+  // the stages, and afterwards the output tile, 128 rows of 256 bytes at a
+  // time (the 256-row tile goes out in two passes, so that its LDS stays at
+  // the two stages' 48 KB and three workgroups share a CU)
+  constexpr int kEpiRows = kTM < 128 ? kTM : 128;
+  constexpr int kSmem = kNStages * kStageBytes > kEpiRows * kWRow ? kNStages * kStageBytes : kEpiRows * kWRow;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   const int n = args.n, kdim = args.k, groups = args.groups;
 
@@ -161,7 +164,9 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
     const bool full = cols == kTK;  // workgroup-uniform
 #pragma unroll
     for (int i = 0; i < kXDma; ++i) {
-      const unsigned off = (full || 8 * xch[i] < cols) ? xdo[i] : kOutOfRange;
+      // (an arithmetic select: a select between the two values compiled to a
+      // select of addresses into the offset array, which then stayed in memory)
+      const unsigned off = xdo[i] | ((full || 8 * xch[i] < cols) ? 0u : kOutOfRange);
       dma16(rx, off, sb + (unsigned)(((kTM / 4) * wave_u + 16 * i) * kXRow));
     }
 #pragma unroll
@@ -176,14 +181,16 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
   unsigned xoff[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) xoff[s] = (unsigned)((wrow + lq) * kXRow + 16 * ((2 * s + hf) ^ ((lq >> 2) & 3)));
-  unsigned woff[2];
+  // (the 128-byte half h = nb >> 1 is added where it is used: an array indexed
+  // by a wavefront-dependent block number was kept in memory by the compiler)
+  unsigned woff_base;
+  int wsel;
   {
     const int gi = lane >> 4, j = lane & 15;
     const int c_lane = 2 * (gi & 1) + ((j & 3) >> 1);
     const int kr_lane = 8 * (gi >> 1) + (j >> 2);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)  // h = nb >> 1
-      woff[h] = (unsigned)(kXBytes + kr_lane * kWRow + 16 * (c_lane ^ (j >> 2)) + 8 * (j & 1) + 128 * (h ^ (gi >> 1)));
+    woff_base = (unsigned)(kXBytes + kr_lane * kWRow + 16 * (c_lane ^ (j >> 2)) + 8 * (j & 1));
+    wsel = gi >> 1;
   }
 
   f32x16 acc[kNB][2] = {};  // [n block][m block], Y^T layout
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
         const int col_nb = wcol / 32 + nb;  // 32-column block within the tile
-        const lds_char* wp = (const lds_char*)(size_t)(sb + woff[col_nb >> 1]);
+        const lds_char* wp = (const lds_char*)(size_t)(sb + woff_base + 128u * (unsigned)(((col_nb >> 1) ^ wsel) & 1));
         const v4i16 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) v4i16*)(wp + 16 * s * kWRow + 64 * (col_nb & 1)));
         const v4i16 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -233,10 +240,9 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
   // 256-byte row, where the accumulator layout would have each store
   // instruction touch 32 rows with 32 bytes each.
   const bf16* Bias = static_cast<const bf16*>(g.bias);
-  __syncthreads();  // every wavefront is done reading the stages
+  unsigned w[kNB][2][4][2];  // packed bf16 outputs: [n block][m block][group][pair]
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const int row = wrow + 32 * mb + lq;
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       f32x16 v = acc[nb][mb];
@@ -257,28 +263,39 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[r] = __builtin_fmaxf(v[r], 0.f);
       }
-      unsigned w[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        w[q][0] = pack_bf16(v[4 * q], v[4 * q + 1]);
-        w[q][1] = pack_bf16(v[4 * q + 2], v[4 * q + 3]);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 chunk = gather_row_chunk(w[2 * t][0], w[2 * t][1], w[2 * t + 1][0], w[2 * t + 1][1]);
-        const int c = (wcol + 32 * nb + 16 * t + 8 * hf) >> 3;
-        *reinterpret_cast<u32x4*>(smem + row * kWRow + 16 * (c ^ (row & 15))) = chunk;
+        w[nb][mb][q][0] = pack_bf16(v[4 * q], v[4 * q + 1]);
+        w[nb][mb][q][1] = pack_bf16(v[4 * q + 2], v[4 * q + 3]);
       }
     }
   }
-  __syncthreads();
-  {
+  constexpr int kPasses = kTM / kEpiRows;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    __syncthreads();  // every wavefront is done reading the stages (or the previous pass's rows)
+    if (wrow / kEpiRows == pass) {  // wave-uniform
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = wrow - kEpiRows * pass + 32 * mb + lq;
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const u32x4 chunk = gather_row_chunk(w[nb][mb][2 * t][0], w[nb][mb][2 * t][1], w[nb][mb][2 * t + 1][0],
+                                                 w[nb][mb][2 * t + 1][1]);
+            const int c = (wcol + 32 * nb + 16 * t + 8 * hf) >> 3;
+            *reinterpret_cast<u32x4*>(smem + row * kWRow + 16 * (c ^ (row & 15))) = chunk;
+          }
+      }
+    }
+    __syncthreads();
     const int c = tid & 15;
 #pragma unroll
-    for (int i = 0; i < kTM / 16; ++i) {
-      const int r = (tid >> 4) + 16 * i;
-      if (r < valid_m && 8 * c < valid_n)
-        *reinterpret_cast<u32x4*>(Y + (int64_t)(m0 + r) * g.ldy + n0 + 8 * c) =
+    for (int i = 0; i < kEpiRows / 16; ++i) {
+      const int r = (tid >> 4) + 16 * i, gr = kEpiRows * pass + r;
+      if (gr < valid_m && 8 * c < valid_n)
+        *reinterpret_cast<u32x4*>(Y + (int64_t)(m0 + gr) * g.ldy + n0 + 8 * c) =
             *reinterpret_cast<const u32x4*>(smem + r * kWRow + 16 * (c ^ (r & 15)));
     }
   }
@@ -289,12 +306,13 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream) {
   int max_m = 0;
   for (int i = 0; i < a.groups; ++i) max_m = a.g[i].m > max_m ? a.g[i].m : max_m;
   const int tiles_n = (a.n + kTN - 1) / kTN;
-  // the tile height whose workgroup count fills whole rounds of 512 best (the
-  // 256-row tile's residency, two per CU by its 64 KB of LDS; the 128-row
-  // tile, 32 KB, fits five); ties go to the 128-row tile
+  // the tile height whose workgroup count fills whole rounds of resident
+  // workgroups best: the 256-row tile (48 KB of LDS, 164 VGPRs) is resident
+  // three per CU, 768 per round, the 128-row tile (32 KB, 95 VGPRs) five per
+  // CU, 1280 per round; ties go to the 128-row tile
   const int64_t big = (int64_t)tiles_n * ((max_m + 255) / 256) * a.groups;
   const int64_t small = (int64_t)tiles_n * ((max_m + 127) / 128) * a.groups;
-  auto fill = [](int64_t wgs) { return (double)wgs / (double)(((wgs + 511) / 512) * 512); };
+  auto fill = [](int64_t wgs, int64_t round) { return (double)wgs / (double)(((wgs + round - 1) / round) * round); };
   if (small < 256) {
     // fewer 128-row workgroups than CUs: 64-row tiles put twice as many in
     // flight (128 x 512 x 512 x 3: 6.8 against 8.0 us; 1000 x 264 x 200 x 2:
@@ -302,7 +320,7 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream) {
     const int tiles_m = (max_m + 63) / 64;
     const dim3 grid((unsigned)(tiles_n * tiles_m * a.groups));
     hipLaunchKernelGGL((linear_bf16_kernel<64>), grid, dim3(256), 0, stream, a, tiles_n, tiles_m);
-  } else if (big >= 512 && fill(big) > fill(small)) {
+  } else if (big >= 768 && fill(big, 768) > fill(small, 1280)) {
     const int tiles_m = (max_m + 255) / 256;
     hipLaunchKernelGGL((linear_bf16_kernel<256>), dim3((unsigned)big), dim3(256), 0, stream, a, tiles_n, tiles_m);
   } else {
