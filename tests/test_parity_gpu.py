@@ -415,6 +415,9 @@ PADDED = [
     # 64 query rows per wavefront (whole 256-row workgroups) under per-item lengths:
     # 0, below one slab, not a multiple of 64, full
     (4, 2, 512, 512, False, "bf16", [512, 300, 37, 0]),
+    # the hand-scheduled loop over exactly one tile (150 and 129 keys: tile 1 is both its first and last
+    # tile, a ragged tile follows for 150), and not at all (64 keys: only the first tile)
+    (3, 2, 512, 512, False, "bf16", [150, 64, 129]),
     (1, 2, 4096, 4096, True, "bf16", [1000]),
     (2, 1, 4096, 4096, True, "bf16", [4096, 2100]),
     # the causal 32-row form under the same kind of lengths, 0 and below one slab included
