@@ -141,13 +141,9 @@ def slot_pairs(x, j):
     return ops
 
 
-def pairs_done_by_check():
-    # after slots 0..3: fma 0..3, exp 0..2, pack 0..1
-    return {"f": 4, "e": 3, "c": 2}
-
-
 def finish_pairs(x):
-    """All weight work of block x that slots 4..7 and the tail would have done."""
+    """All weight work of block x that slots 4..7 and the tail would have done
+    (by the check, slots 0..3 have issued fma 0..3, exp 0..2 and pack 0..1)."""
     ops = []
     ops += pair_ops(x, 3, "e")
     for i in range(4, 8):
@@ -199,7 +195,7 @@ def s_mfma(xn, kbuf, kk):
     return mfma32(S[xn], KB[kbuf] + 4 * kk, Q[xn] + 4 * kk, "0" if kk == 0 else vr(S[xn], 16))
 
 
-def dma_tile(stage, uid):
+def dma_tile(stage):
     """DMA of the next tile (4 loads per wavefront) into `stage`; the caller
     has checked that the tile exists."""
     ops = [
@@ -255,7 +251,7 @@ def tile_sync(stage, uid):
         "s_barrier",
         f"s_cmp_lt_i32 s{S_X}, 5",
         f"s_cbranch_scc1 {uid}_nodma",
-    ] + dma_tile(stage, uid) + [f"{uid}_nodma:"]
+    ] + dma_tile(stage) + [f"{uid}_nodma:"]
 
 
 def rare_fix(e, y, kbuf_prev, tmp_scores, back):
@@ -341,9 +337,6 @@ def step(e, cold, stage, p, kind):
     if has_prev:
         e(f"v_cmp_nge_f32_e32 vcc, {MAX_SUM}, {v(RS)}",
           f"s_cbranch_vccnz {uid}_rare")
-    # continuation point (main path)
-    post = []   # what follows the P V products and the row sums
-
     def loads_and_sync():
         ops = []
         if p == 0:
@@ -367,8 +360,8 @@ def step(e, cold, stage, p, kind):
         if has_prev:
             e(pv_mfma(y, vbuf_prev, j - 4))
         e(*slot_pairs(x, j))
-        if j == 4:
-            e(*post[: len(post) if p != 2 else 0])  # LDS reads early; the sync comes after the products
+        if j == 4 and p != 2:
+            e(*post)  # the fragment reads go early; p = 2's sync waits until after the row sums
     # tail: last weights, then the row-sum products of unit u
     e(*pair_ops(x, 7, "e"))
     e(*pair_ops(x, 6, "c"))
