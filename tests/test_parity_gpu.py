@@ -307,8 +307,10 @@ LINEAR_CASES = [
     # 64-row tiles (grids smaller than the CU count), ragged m, n and k
     (1, 8, 8, "bf16"), (300, 136, 72, "bf16"), (2048, 512, 512, "bf16"), (257, 520, 136, "bf16"),
     (1000, 1536, 512, "bf16"), (64, 128, 1040, "bf16"),
-    # 128-row tiles
-    (16384, 512, 512, "bf16"), (4100, 1096, 200, "bf16"), (8000, 2048, 520, "bf16"), (32640, 512, 512, "bf16"),
+    # 128-row tiles; grids of at most 512 of them (two per CU) take the 4-stage ring with two k chunks per
+    # barrier: 16 chunks, 7 (an odd count, ragged last), 1 and 2 (both ragged)
+    (16384, 512, 512, "bf16"), (4100, 1096, 200, "bf16"), (8200, 512, 24, "bf16"), (8200, 512, 40, "bf16"),
+    (8000, 2048, 520, "bf16"), (32640, 512, 512, "bf16"),
     # 256-row tiles: 768 workgroups fill one round, with ragged m (the epilogue's
     # second pass partly or wholly past the end) and a partial last k chunk
     (12200, 2048, 520, "bf16"), (49000, 512, 512, "bf16"), (12161, 2048, 512, "bf16"),

@@ -94,20 +94,24 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {
 // blocks). kTM = 128: wavefronts form 2 x 2, each 64 rows x 64 columns.
 // kTM = 64: wavefront w owns all 64 rows and columns 32w..+31.
 // LDS stage: X tile (kTM rows x 64 B), then W tile (32 k-rows x 256 B).
-template <int kTM>
+// kPair: a 4-stage ring, two chunks loaded and multiplied per barrier (for
+// grids of at most two workgroups per CU, where the deeper ring costs no
+// residency).
+template <int kTM, bool kPair = false>
 __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, int tiles_n, int tiles_m) {
   constexpr int kWM = kTM / 64;         // wavefronts along m
   constexpr int kWC = 128 / (4 / kWM);  // columns per wavefront
   constexpr int kNB = kWC / 32;         // 32-column MFMA blocks per wavefront
   constexpr int kXBytes = kTM * kXRow;
   constexpr int kStageBytes = kXBytes + kTK * kWRow;
+  constexpr int kStages = kPair ? 4 : kNStages;
   constexpr int kXDma = kTM / 64;  // X loads per wavefront per chunk (16 rows of 64 B each)
   constexpr int kWDma = 2;         // W loads per wavefront per chunk (4 rows of 256 B each)
   // the stages, and afterwards the output tile, 128 rows of 256 bytes at a
   // time (the 256-row tile goes out in two passes, so that its LDS stays at
   // the two stages' 48 KB and three workgroups share a CU)
   constexpr int kEpiRows = kTM < 128 ? kTM : 128;
-  constexpr int kSmem = kNStages * kStageBytes > kEpiRows * kWRow ? kNStages * kStageBytes : kEpiRows * kWRow;
+  constexpr int kSmem = kStages * kStageBytes > kEpiRows * kWRow ? kStages * kStageBytes : kEpiRows * kWRow;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   const int n = args.n, kdim = args.k, groups = args.groups;
 
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
     const int cols = min(kTK, kdim - k0);
     const u32x4 rx = make_rsrc(X + k0, (unsigned)(((valid_m - 1) * ldx + cols) * 2));
     const u32x4 rw = make_rsrc(W + (int64_t)k0 * ldw, (unsigned)(((cols - 1) * ldw + valid_n) * 2));
-    const unsigned sb = smem_base + (unsigned)((c % kNStages) * kStageBytes);
+    const unsigned sb = smem_base + (unsigned)((c % kStages) * kStageBytes);
     const bool full = cols == kTK;  // workgroup-uniform
 #pragma unroll
     for (int i = 0; i < kXDma; ++i) {
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
 
   f32x16 acc[kNB][2] = {};  // [n block][m block], Y^T layout
   auto compute = [&](int c) {
-    const unsigned sb = smem_base + (unsigned)((c % kNStages) * kStageBytes);
+    const unsigned sb = smem_base + (unsigned)((c % kStages) * kStageBytes);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 xf[2], wf[kNB];
@@ -224,11 +228,25 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(LinearArgs args, in
   // Chunk c: wait for its loads, barrier (which also ends every read of the
   // stage chunk c + 1 reuses), start the loads of chunk c + 1, multiply.
   const int nchunks = (kdim + kTK - 1) / kTK;
-  dma_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (c + 1 < nchunks) dma_chunk(c + 1);
-    compute(c);
+  if constexpr (!kPair) {
+    dma_chunk(0);
+    for (int c = 0; c < nchunks; ++c) {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (c + 1 < nchunks) dma_chunk(c + 1);
+      compute(c);
+    }
+  } else {
+    // chunks c and c + 1 per barrier; the barrier also ends every read of the
+    // stages that chunks c + 2 and c + 3 reuse
+    dma_chunk(0);
+    if (1 < nchunks) dma_chunk(1);
+    for (int c = 0; c < nchunks; c += 2) {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (c + 2 < nchunks) dma_chunk(c + 2);
+      if (c + 3 < nchunks) dma_chunk(c + 3);
+      compute(c);
+      if (c + 1 < nchunks) compute(c + 1);
+    }
   }
 
   // Epilogue. A lane holds row wrow + 32*mb + lq and columns wcol + 32*nb +
@@ -323,6 +341,11 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream) {
   } else if (big >= 768 && fill(big, 768) > fill(small, 1280)) {
     const int tiles_m = (max_m + 255) / 256;
     hipLaunchKernelGGL((linear_bf16_kernel<256>), dim3((unsigned)big), dim3(256), 0, stream, a, tiles_n, tiles_m);
+  } else if (small <= 512) {
+    // at most two workgroups per CU: the 4-stage ring costs no residency
+    const int tiles_m = (max_m + 127) / 128;
+    const dim3 grid((unsigned)(tiles_n * tiles_m * a.groups));
+    hipLaunchKernelGGL((linear_bf16_kernel<128, true>), grid, dim3(256), 0, stream, a, tiles_n, tiles_m);
   } else {
     const int tiles_m = (max_m + 127) / 128;
     const dim3 grid((unsigned)(tiles_n * tiles_m * a.groups));
