@@ -46,8 +46,9 @@
 // tile whose first key lies past the wavefront's last query is skipped; only
 // tiles that straddle the diagonal (or the ragged end) apply per-element masks.
 // Causal workgroups run heaviest query block first, with each head's blocks
-// on one XCD (the 32-row causal form puts the lightest levels first when its
-// grid overflows one round of resident workgroups by at most a round).
+// on one XCD (when the grid overflows one round of resident workgroups by at
+// most a round, the 32-row causal form puts as many of the lightest levels
+// first as overflow, the 64-row form the lightest quarter of its levels).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -646,7 +647,7 @@ __device__ __forceinline__ void attend_slab(RowState (&st)[2], const u32x4 (&qf)
 }
 
 template <bool kCausal>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r64(AttnArgs a, float c, unsigned q_sign, int n_qblk) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r64(AttnArgs a, float c, unsigned q_sign, int n_qblk, int n_light) {
   constexpr int kRowsPerWave = 64;
   constexpr int kRows = 256;
   __shared__ __attribute__((aligned(16))) char smem[kNStages * kStageBytes];
@@ -660,18 +661,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_d64_r64(AttnArgs a, floa
 
   int bh, qblk;
   if (kCausal) {
-    // heaviest query blocks (most key tiles) are dispatched first; workgroup i
-    // goes to XCD i % 8, so XCD x takes the heads bh = x (mod 8) and all of a
-    // head's query blocks share one L2
+    // dispatch level r of the query blocks: the n_light lightest levels first,
+    // then the others heaviest first (most key tiles); workgroup i goes to
+    // XCD i % 8, so XCD x takes the heads bh = x (mod 8) and all of a head's
+    // query blocks share one L2
     const int BH = a.batch * a.heads;
+    int r;
     if ((BH & 7) == 0) {
       const int x = blockIdx.x & 7, j = blockIdx.x >> 3, bhx = BH >> 3;
-      qblk = n_qblk - 1 - j / bhx;
+      r = j / bhx;
       bh = x + 8 * (j % bhx);
     } else {
-      qblk = n_qblk - 1 - (int)(blockIdx.x / BH);
+      r = (int)(blockIdx.x / BH);
       bh = (int)(blockIdx.x % BH);
     }
+    qblk = r < n_light ? n_light - 1 - r : n_qblk - 1 - (r - n_light);
   } else {
     const int total = gridDim.x, id = blockIdx.x;
     const int per = total >> 3, rem = total & 7, x = id & 7, slot = id >> 3;
@@ -1161,13 +1165,40 @@ static void launch_r32d(const AttnArgs& a, hipStream_t stream, float c, unsigned
     hipLaunchKernelGGL((attn_fwd_bf16_d64_r32d<false>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk, 0);
 }
 
+// Workgroups of the causal 64-row form the current device holds at once
+// (occupancy x compute units), cached per device; 0 if the query fails.
+static int r64_resident() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] != 0) return cache[dev] > 0 ? cache[dev] : 0;
+  int occ = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_fwd_bf16_d64_r64<true>, 256, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || occ * cus <= 0) {
+    cache[dev] = -1;
+    return 0;
+  }
+  cache[dev] = occ * cus;
+  return cache[dev];
+}
+
 static void launch_slab(const AttnArgs& a, hipStream_t stream, float c, unsigned q_sign) {
   const int n_qblk = (a.n_q + 255) / 256;
-  const dim3 grid((unsigned)(n_qblk * a.batch * a.heads));
+  const int n_items = n_qblk * a.batch * a.heads;
+  const dim3 grid((unsigned)n_items);
+  // Causal grids of more than one and at most two rounds of resident
+  // workgroups: the lightest quarter of the query-block levels goes first.
+  // Measured on the long causal launch (2 x 16 heads, N = 8192: 32 levels,
+  // two rounds of 512): 8 levels first 253-262 against 261-269 us on two
+  // boxes; the dependence on the count is not smooth (6, 7 and 10 were
+  // slower than none), and grids of four rounds gained nothing.
+  int n_light = 0;
+  const int resident = a.causal ? r64_resident() : 0;
+  if (resident > 0 && n_items > resident && n_items <= 2 * resident) n_light = n_qblk / 4;
   if (a.causal)
-    hipLaunchKernelGGL((attn_fwd_bf16_d64_r64<true>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r64<true>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk, n_light);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_d64_r64<false>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk);
+    hipLaunchKernelGGL((attn_fwd_bf16_d64_r64<false>), grid, dim3(256), 0, stream, a, c, q_sign, n_qblk, 0);
 }
 
 }  // namespace
